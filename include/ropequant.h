@@ -1,0 +1,174 @@
+/*
+ * libropequant - fused RoPE + block-FP8 steps around DeepSeek-V4-style
+ * 512-dim attention heads, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] "vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선"
+ *        (analysis of vLLM PR #49236): section 1 defines the fused q-norm/RoPE
+ *        and kv-RoPE/quant/insert op with a caller-allocated q_out and lists its
+ *        argument checks; section 2 gives its schema (outputs mutated, returns
+ *        nothing).
+ *   [P3] "vLLM, DeepSeek V4 모델의 저지연을 위한 RMSNorm과 라우터 GEMV 연산
+ *        융합으로 성능 극대화" (analysis of vLLM PR #41263): section 5 gives the
+ *        RMSNorm formula.
+ *   [P4] "한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE +
+ *        FP8 quant 커널 3.5배 가속기" (analysis of vLLM PR #63540): intro (the
+ *        op sits before the wo_a projection), section 1 (heads grouped per
+ *        wo_a group, scale column = head_in_group * 4 + block), section 2 (the
+ *        GPT-J inverse rotation), section 3 (block-128 amax, UE8M0 packing).
+ *   [P5] "vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput
+ *        향상" (analysis of vLLM PR #46862): section 1 (power-of-two scale).
+ *
+ * Common conventions
+ *   - Head vectors are 512 dims: dims 0..447 are not rotated, dims 448..511
+ *     are rotated GPT-J style, in adjacent pairs (2k, 2k+1), k = 224..255.
+ *   - cos_sin_cache is fp32 [max_pos, 64], row-major: row p holds cos in
+ *     columns 0..31 and sin in columns 32..63; pair k uses column k-224 and
+ *     32+k-224 of row positions[t].  It must be 16-byte aligned.
+ *   - bf16 values are passed as their uint16_t bit patterns; e4m3 codes as
+ *     uint8_t (OCP E4M3: bias 7, max 448, no infinities, 0x7F/0xFF NaN).
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees, synchronizes or keeps state; it is
+ *     reentrant.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and the call returns without waiting.
+ *   - Return value: RQ_OK (0) or a negative RQ_ERR_* status.  On any error
+ *     nothing is launched and no output byte is touched.  n_tokens == 0
+ *     returns RQ_OK with no launch (pointers are then not inspected).
+ *   - Device data is not read by the host.  Caller contract: positions in
+ *     [0, max_pos); slots unique and below num_blocks * cache_block_size;
+ *     input values finite (and |q| < 2^59 for qnorm_rope).  The kernels never
+ *     access memory outside the described tensors even when the contract is
+ *     broken: a unit whose position is out of range is written as NaN (e4m3
+ *     0x7F codes with NaN scales, or bf16 0x7FC0), and a slot outside
+ *     [0, num_blocks * cache_block_size) is skipped.
+ *   - Strides are in elements of the tensor's own type unless "bytes" is said.
+ *   - Arithmetic: every fp32 step is an IEEE-754 basic operation rounded to
+ *     nearest even, with no fused multiply-add; division and square root are
+ *     correctly rounded; denormals are kept.
+ */
+#ifndef ROPEQUANT_H
+#define ROPEQUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROPEQUANT_ABI_VERSION 1
+
+enum {
+  RQ_OK = 0,
+  RQ_ERR_NULL = -1,   /* a required pointer is NULL */
+  RQ_ERR_SHAPE = -2,  /* a size is out of range or inconsistent */
+  RQ_ERR_STRIDE = -3, /* a stride is non-positive or lets outputs overlap */
+  RQ_ERR_ALIGN = -4,  /* a pointer or stride breaks the required alignment */
+  RQ_ERR_VALUE = -5,  /* a scalar argument (scale_fmt, eps) is invalid */
+  RQ_ERR_HIP = -6     /* the HIP runtime refused the launch */
+};
+
+enum {
+  RQ_SCALE_FP32 = 0,  /* one fp32 scale per 128-dim block: amax / 448 */
+  RQ_SCALE_UE8M0 = 1  /* power-of-two scale, exponent byte per block */
+};
+
+/*
+ * inv_rope_fp8_quant - inverse RoPE, then block-128 FP8 quantization, of the
+ * attention output before the grouped wo_a projection ([P4] intro, sections
+ * 1-3).  For every token t < n_tokens and head h < n_heads:
+ *   x   = fp32(o[t, h, :])
+ *   x'  = x with pairs k >= 224 rotated back:  e' = e*c + o*s,  o' = o*c - e*s
+ *   m_b = max(max_{i in block b} |x'_i|, eps)            (b = 0..3)
+ *   RQ_SCALE_FP32 : s_b = m_b / 448;  codes = e4m3_rne(x' * (1 / s_b))
+ *   RQ_SCALE_UE8M0: k_b = smallest integer with 2^k_b >= m_b / 448;
+ *                   codes = e4m3_rne(x' * 2^-k_b)
+ * with g = h / heads_per_group, j = h % heads_per_group:
+ *   out   [g*out_stride_group + t*out_stride_token + j*512 + d]  (bytes)
+ *   FP32  scales (float*)   [g*sc_stride_group + t*sc_stride_token + (j*4+b)*sc_stride_block] = s_b
+ *   UE8M0 scales (uint32_t*)[g*sc_stride_group + t*sc_stride_token + j*sc_stride_block]
+ *         = sum_b (k_b + 127) << (8*b)      (block b in byte b)
+ * Default (group-major, what wo_a consumes) layout: out [G, N, hpg*512] with
+ * strides (N*hpg*512, hpg*512); FP32 scales [G, N, hpg*4] with strides
+ * (N*hpg*4, hpg*4, 1); UE8M0 scales [G, N, hpg] with strides (N*hpg, hpg, 1).
+ * Token-major [N, H, 512] is out strides (hpg*512, H*512).
+ *
+ * o: bf16 [N, H, 512] with strides (o_stride_token, o_stride_head, 1); base
+ *    16-byte aligned, strides positive multiples of 8.
+ * positions: int64 [N].  eps: amax floor (>= 2^-116 as fp32; vLLM-style
+ *    default 1e-10).  out: 16-byte aligned, strides positive multiples of 16,
+ *    rows must not overlap.  scales: 4-byte aligned, positive strides, no two
+ *    scales may share an address.  n_tokens * n_heads < 2^31.
+ */
+int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
+                       const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                       int64_t n_tokens, int32_t n_heads, int32_t heads_per_group,
+                       int32_t scale_fmt, double eps,
+                       uint8_t* out, int64_t out_stride_group, int64_t out_stride_token,
+                       void* scales, int64_t sc_stride_group, int64_t sc_stride_token,
+                       int64_t sc_stride_block, void* stream);
+
+/*
+ * qnorm_rope - per-head RMSNorm and forward RoPE of the queries, written into
+ * a head-padded output whose pad heads are zero ([P1] section 1: q_out is
+ * preallocated by the caller, every element is written so it may be
+ * uninitialized, q_head_padded >= num_heads_q; [P3] section 5: RMSNorm).
+ * For t < n_tokens, h < n_heads_q:
+ *   x  = fp32(q_in[t, h, :])
+ *   ss = sum of x_d^2 in a fixed order: 64 chunks of 8 consecutive dims, each
+ *        summed left to right; then 6 butterfly rounds, chunk c adding chunk
+ *        c xor k for k = 1, 2, 4, 8, 16, 32
+ *   r  = 1 / sqrt(ss * (1/512) + eps)
+ *   y  = (x * r) * w   (w = fp32(norm_weight), or y = x * r if norm_weight is NULL)
+ *   y' = y with pairs k >= 224 rotated forward:  e' = e*c - o*s,  o' = o*c + e*s
+ *   q_out[t, h, :] = bf16_rne(y')
+ * and q_out[t, h, :] = +0 (0x0000) for n_heads_q <= h < q_head_padded.
+ * q_in: bf16 [N, Hq, 512], strides (q_stride_token, q_stride_head, 1), base
+ *   16-byte aligned, strides positive multiples of 8.  norm_weight: bf16
+ *   [512] or NULL, 16-byte aligned.  q_out: bf16 [N, q_head_padded, 512]
+ *   contiguous, 16-byte aligned.  eps: RMSNorm epsilon (> 0, fp32-finite).
+ *   n_tokens * q_head_padded < 2^31.
+ */
+int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+               const uint16_t* norm_weight, const int64_t* positions,
+               const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+               int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
+               void* stream);
+
+/*
+ * kv_rope_quant_insert - forward RoPE and block-128 FP8 quantization of the
+ * shared 512-dim kv vector, inserted into a paged uint8 cache through
+ * slot_mapping ([P1] section 1: k_cache [num_blocks, block_bytes] uint8,
+ * slot_mapping [N] int64, cache_block_size, per-block stride).
+ * For t < n_tokens with s = slot_mapping[t] >= 0:
+ *   x' = forward RoPE of fp32(kv[t, :]); codes and block scales as in
+ *        inv_rope_fp8_quant
+ *   record = k_cache + (s / cache_block_size) * block_stride_bytes
+ *                    + (s % cache_block_size) * 528
+ *   record[0..511]   = the 512 e4m3 codes
+ *   RQ_SCALE_FP32 : record[512..527] = s_0..s_3 as little-endian fp32
+ *   RQ_SCALE_UE8M0: record[512..515] = exponent bytes k_b + 127 (block b at
+ *                   byte 512+b), record[516..527] = 0
+ * s < 0 skips the token (padding).  No other byte of k_cache is written.
+ * kv: bf16 [N, 512], row stride kv_stride_token (positive multiple of 8),
+ *   16-byte aligned.  k_cache: 16-byte aligned; block_stride_bytes a multiple
+ *   of 16 and >= cache_block_size * 528; num_blocks * cache_block_size < 2^31.
+ *   Slots must be unique (duplicates race).
+ */
+int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
+                         const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                         const int64_t* slot_mapping, int64_t n_tokens,
+                         uint8_t* k_cache, int64_t num_blocks, int64_t block_stride_bytes,
+                         int32_t cache_block_size, int32_t scale_fmt, double eps,
+                         void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ropequant_strerror(int status);
+
+/* ROPEQUANT_ABI_VERSION of the loaded library. */
+int ropequant_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPEQUANT_H */

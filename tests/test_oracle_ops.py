@@ -1,0 +1,230 @@
+"""Pins for the oracle's whole ops: layout, padding, cache placement, glue.
+
+The head steps are pinned in test_oracle_steps.py; here the ops are checked
+for how they place results (index maps rebuilt with numpy reshapes and
+transposes), for the pad and untouched-byte guarantees, for batch invariance,
+against fp64 end-to-end references, and for their error returns.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from rope_fp8_quant_amd import synth
+from tests.helpers import bf16_value, e4m3_ulp, f32_bits, rope_angles
+
+
+def _identity_cache(max_pos):
+    c = np.zeros((max_pos, 64), np.float32)
+    c[:, :32] = 1.0
+    return c
+
+
+# ------------------------------------------------------------------- IRQ
+
+@pytest.mark.parametrize("H,hpg", [(8, 8), (32, 8), (48, 6), (24, 4), (6, 3)])
+def test_irq_layout_identifies_every_head(H, hpg):
+    # Head (t, h) is the constant v(t, h) = (t*H + h + 1) / 8 in every dim; with
+    # an identity cos/sin table every block's amax is v, so its codes are all
+    # 0x7E and its scale is v/448.  The expected scale tensor is built with
+    # numpy reshapes only: [N, H, 4] -> [N, G, hpg, 4] -> [G, N, hpg*4].
+    N = 5
+    G = H // hpg
+    v = (np.arange(N * H, dtype=np.float32).reshape(N, H) + 1) / 8
+    o = synth.f32_to_bf16_bits(np.repeat(v[:, :, None], 512, axis=2))
+    pos = np.arange(N, dtype=np.int64)
+    out, sc = oracle.inv_rope_fp8_quant(o, pos, _identity_cache(8), hpg)
+    assert (out == 0x7E).all()
+    s = np.repeat((v / np.float32(448))[:, :, None], 4, axis=2)
+    expect = s.reshape(N, G, hpg, 4).transpose(1, 0, 2, 3).reshape(G, N, hpg * 4)
+    assert (f32_bits(sc) == f32_bits(expect)).all()
+
+
+def test_irq_layout_codes_follow_heads():
+    # Distinct per-head sign patterns make every head's code row unique.
+    N, H, hpg = 3, 8, 4
+    rng = np.random.default_rng(0)
+    sgn = rng.choice([-1.0, 1.0], size=(N, H, 512)).astype(np.float32)
+    o = synth.f32_to_bf16_bits(sgn)
+    out, _ = oracle.inv_rope_fp8_quant(o, np.zeros(N, np.int64), _identity_cache(1), hpg)
+    codes = np.where(sgn > 0, 0x7E, 0xFE).astype(np.uint8)
+    expect = codes.reshape(N, H // hpg, hpg * 512).transpose(1, 0, 2)
+    assert (out == expect).all()
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_FP32, oracle.SCALE_UE8M0])
+def test_irq_token_major_is_group_major_permuted(fmt):
+    cfg = dict(synth.IRQ_TINY, N=7, H=12, hpg=6)
+    o, pos, cache = synth.irq_inputs(cfg)
+    G = 2
+    og, sg = oracle.inv_rope_fp8_quant(o, pos, cache, 6, fmt, layout="group")
+    ot, st = oracle.inv_rope_fp8_quant(o, pos, cache, 6, fmt, layout="token")
+    assert (ot.reshape(7, G, 6 * 512).transpose(1, 0, 2) == og).all()
+    per = 4 * 6 if fmt == oracle.SCALE_FP32 else 6
+    assert (st.reshape(7, G, per).transpose(1, 0, 2) == sg).all()
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_FP32, oracle.SCALE_UE8M0])
+def test_irq_is_rope_then_quant_per_head(fmt):
+    o, pos, cache = synth.irq_inputs(synth.IRQ_TINY)
+    out, sc = oracle.inv_rope_fp8_quant(o, pos, cache, 8, fmt)
+    for t in range(o.shape[0]):
+        for h in range(8):
+            x = bf16_value(o[t, h])
+            codes, s4, word = oracle.quant_head(oracle.rope_head(x, cache[pos[t]], True), fmt)
+            assert (out[0, t, h * 512:(h + 1) * 512] == codes).all()
+            if fmt == oracle.SCALE_FP32:
+                assert (f32_bits(sc[0, t, 4 * h:4 * h + 4]) == f32_bits(s4)).all()
+            else:
+                assert sc[0, t, h] == word
+
+
+def test_irq_end_to_end_fp64_bound():
+    # Dequantized output vs fp64 inverse rotation of the input, with angles
+    # from the frequency definition (not the table).
+    o, pos, cache = synth.irq_inputs(synth.IRQ_TINY)
+    out, sc = oracle.inv_rope_fp8_quant(o, pos, cache, 8)
+    ang = rope_angles(pos)
+    for t in range(o.shape[0]):
+        for h in range(8):
+            x = bf16_value(o[t, h]).astype(np.float64)
+            z = (x[448::2] + 1j * x[449::2]) * np.exp(-1j * ang[t])
+            ref = x.copy()
+            ref[448::2], ref[449::2] = z.real, z.imag
+            s = np.repeat(sc[0, t, 4 * h:4 * h + 4].astype(np.float64), 128)
+            deq = oracle.e4m3_to_f32(out[0, t, h * 512:(h + 1) * 512]) * s
+            bound = 0.5 * e4m3_ulp(ref / s) * s + 2.0 ** -20 * np.abs(ref) + 1e-12
+            assert (np.abs(deq - ref) <= bound).all()
+
+
+def test_irq_batch_invariance():
+    o, pos, cache = synth.irq_inputs(dict(synth.IRQ_TINY, N=9))
+    full, fsc = oracle.inv_rope_fp8_quant(o, pos, cache, 8)
+    for t in (0, 4, 8):
+        one, osc = oracle.inv_rope_fp8_quant(o[t:t + 1].copy(), pos[t:t + 1].copy(), cache, 8)
+        assert (one[:, 0] == full[:, t]).all()
+        assert (f32_bits(osc[:, 0]) == f32_bits(fsc[:, t])).all()
+
+
+def test_irq_rejects_bad_arguments():
+    o, pos, cache = synth.irq_inputs(synth.IRQ_TINY)
+    with pytest.raises(oracle.OracleError):
+        oracle.inv_rope_fp8_quant(o, pos, cache, 3)  # 8 % 3 != 0
+    bad = pos.copy()
+    bad[2] = cache.shape[0]
+    with pytest.raises(oracle.OracleError):
+        oracle.inv_rope_fp8_quant(o, bad, cache, 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.inv_rope_fp8_quant(o, pos, cache, 8, eps=0.0)
+
+
+# ------------------------------------------------------------------- QNR
+
+def test_qnr_pad_heads_exact_zero_and_live_heads_composed():
+    cfg = dict(synth.QNR_FORWARD, N=3, Hq=4, Hpad=7)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    out = oracle.qnorm_rope(q, w, pos, cache, 7, 1e-6)
+    assert (out[:, 4:] == 0).all()
+    for t in range(3):
+        for h in range(4):
+            y = oracle.rmsnorm_head(bf16_value(q[t, h]), w, 1e-6)
+            z = oracle.rope_head(y, cache[pos[t]], False)
+            assert (out[t, h] == oracle.f32_to_bf16(z)).all()
+
+
+def test_qnr_end_to_end_fp64_within_one_bf16_ulp():
+    cfg = dict(synth.QNR_FORWARD, N=4, Hq=6, Hpad=8)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    out = oracle.qnorm_rope(q, w, pos, cache, 8, 1e-6)
+    ang = rope_angles(pos)
+    wf = bf16_value(w).astype(np.float64)
+    for t in range(4):
+        for h in range(6):
+            x = bf16_value(q[t, h]).astype(np.float64)
+            y = x / np.sqrt(np.mean(x * x) + 1e-6) * wf
+            z = (y[448::2] + 1j * y[449::2]) * np.exp(1j * ang[t])
+            y[448::2], y[449::2] = z.real, z.imag
+            got = bf16_value(out[t, h]).astype(np.float64)
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 1e-30))) - 7)
+            assert (np.abs(got - y) <= ulp).all()
+
+
+def test_qnr_null_weight_is_unit_weight():
+    cfg = dict(synth.QNR_FORWARD, N=2, Hq=3, Hpad=3)
+    q, _, pos, cache = synth.qnr_inputs(cfg)
+    a = oracle.qnorm_rope(q, None, pos, cache, 3, 1e-6)
+    b = oracle.qnorm_rope(q, np.full(512, 0x3F80, np.uint16), pos, cache, 3, 1e-6)
+    assert (a == b).all()
+
+
+def test_qnr_rejects_short_padding():
+    cfg = dict(synth.QNR_FORWARD, N=2, Hq=3, Hpad=3)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    with pytest.raises(oracle.OracleError):
+        oracle.qnorm_rope(q, w, pos, cache, 2, 1e-6)
+
+
+# ------------------------------------------------------------------- KVI
+
+def _small_kvi(N=10, nb=4, bs=4, seed=3, fmt=oracle.SCALE_FP32, holes=()):
+    kv = synth.normal_bf16((N, 512), seed, synth.T_KV)
+    pos = synth.uniform_positions(N, 512, seed)
+    slots = synth.slot_permutation(N, nb * bs, seed)
+    for i in holes:
+        slots[i] = -1
+    cache = synth.cos_sin_cache(512)
+    stride = bs * 528 + 32  # a gap after each block's records
+    k_cache = np.full((nb, stride), 0xAA, np.uint8)
+    oracle.kv_rope_quant_insert(kv, pos, cache, slots, k_cache, bs, stride, fmt)
+    return kv, pos, slots, cache, k_cache, bs, stride
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_FP32, oracle.SCALE_UE8M0])
+def test_kvi_records_land_on_their_slots_only(fmt):
+    kv, pos, slots, cache, k_cache, bs, stride = _small_kvi(fmt=fmt, holes=(2, 7))
+    flat = k_cache.reshape(-1)
+    touched = np.zeros(flat.size, bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        off = (s // bs) * stride + (s % bs) * 528
+        touched[off:off + 528] = True
+        rec = flat[off:off + 528]
+        y = oracle.rope_head(bf16_value(kv[t]), cache[pos[t]], False)
+        codes, s4, word = oracle.quant_head(y, fmt)
+        assert (rec[:512] == codes).all()
+        if fmt == oracle.SCALE_FP32:
+            assert (rec[512:528].view(np.float32) == s4).all()
+        else:
+            assert rec[512:516].view(np.uint32)[0] == word
+            assert (rec[516:528] == 0).all()
+    assert (flat[~touched] == 0xAA).all()
+    assert touched.sum() == 528 * (len(slots) - 2)
+
+
+def test_kvi_dequant_within_bound_of_fp64_rope():
+    kv, pos, slots, cache, k_cache, bs, stride = _small_kvi()
+    ang = rope_angles(pos)
+    flat = k_cache.reshape(-1)
+    for t, s in enumerate(slots):
+        off = (s // bs) * stride + (s % bs) * 528
+        x = bf16_value(kv[t]).astype(np.float64)
+        z = (x[448::2] + 1j * x[449::2]) * np.exp(1j * ang[t])
+        ref = x.copy()
+        ref[448::2], ref[449::2] = z.real, z.imag
+        sc = np.repeat(flat[off + 512:off + 528].view(np.float32).astype(np.float64), 128)
+        deq = oracle.e4m3_to_f32(flat[off:off + 512]) * sc
+        bound = 0.5 * e4m3_ulp(ref / sc) * sc + 2.0 ** -20 * np.abs(ref) + 1e-12
+        assert (np.abs(deq - ref) <= bound).all()
+
+
+def test_kvi_rejects_duplicate_and_out_of_range_slots():
+    kv = synth.normal_bf16((3, 512), 1, synth.T_KV)
+    pos = np.zeros(3, np.int64)
+    cache = synth.cos_sin_cache(4)
+    k_cache = np.zeros((2, 2 * 528), np.uint8)
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_rope_quant_insert(kv, pos, cache, np.array([1, 3, 1], np.int64), k_cache, 2)
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_rope_quant_insert(kv, pos, cache, np.array([0, 1, 4], np.int64), k_cache, 2)
+    # duplicates of the skip marker are fine
+    oracle.kv_rope_quant_insert(kv, pos, cache, np.array([-1, 3, -1], np.int64), k_cache, 2)

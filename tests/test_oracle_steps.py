@@ -1,0 +1,244 @@
+"""Pins for the oracle's per-head steps: RoPE, block FP8 quant, RMSNorm.
+
+Every check here is independent of the oracle's own formulas: fp64 complex
+rotation with angles computed from the RoPE frequency definition, exact
+special tables (cos 0 / sin 1), the inverse-after-forward round trip, the
+dequantization error bound, the block-max-maps-to-448 property, torch's e4m3
+cast on cases where the scale is an exact power of two, an fp64 RMSNorm, and
+hand-derived sums that fix the summation order.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from rope_fp8_quant_amd import synth
+from tests.helpers import bf16_value, e4m3_ulp, f32_bits, rope_angles, torch_e4m3
+
+
+def _head(seed, std=1.0, nonzero=True):
+    x = np.random.default_rng(seed).standard_normal(512).astype(np.float32) * std
+    if nonzero:
+        x[x == 0] = 1.0
+    return x
+
+
+# ------------------------------------------------------------------ RoPE
+
+def test_rope_nope_dims_bit_identical():
+    cache = synth.cos_sin_cache(100)
+    for inverse in (True, False):
+        x = _head(1)
+        y = oracle.rope_head(x, cache[37], inverse)
+        assert (f32_bits(y[:448]) == f32_bits(x[:448])).all()
+        assert not (f32_bits(y[448:]) == f32_bits(x[448:])).all()
+
+
+def test_rope_position_zero_is_identity():
+    cache = synth.cos_sin_cache(4)
+    x = _head(2)
+    for inverse in (True, False):
+        assert (f32_bits(oracle.rope_head(x, cache[0], inverse)) == f32_bits(x)).all()
+
+
+def test_rope_quarter_turn_exact():
+    # cos = 0, sin = 1: rotation by +90 degrees maps (e, o) -> (-o, e);
+    # the inverse maps (e, o) -> (o, -e).  Every product is exact.
+    row = np.concatenate([np.zeros(32), np.ones(32)]).astype(np.float32)
+    x = _head(3)
+    e, o = x[448::2], x[449::2]
+    fwd = oracle.rope_head(x, row, inverse=False)
+    inv = oracle.rope_head(x, row, inverse=True)
+    assert (fwd[448::2] == -o).all() and (fwd[449::2] == e).all()
+    assert (inv[448::2] == o).all() and (inv[449::2] == -e).all()
+
+
+@pytest.mark.parametrize("inverse", [True, False])
+def test_rope_matches_fp64_complex_rotation(inverse):
+    max_pos = 65536
+    positions = np.array([1, 2, 3, 17, 255, 4095, 16383, 40000, 65535])
+    cache = synth.cos_sin_cache(max_pos)
+    ang = rope_angles(positions)  # [P, 32], independent of the table
+    for pi, p in enumerate(positions):
+        x = _head(10 + pi)
+        y = oracle.rope_head(x, cache[p], inverse)
+        z = x[448::2].astype(np.float64) + 1j * x[449::2].astype(np.float64)
+        rot = np.exp((-1j if inverse else 1j) * ang[pi])
+        w = z * rot
+        # Bound: table entries are cos/sin rounded to fp32 (<= 2^-25 each),
+        # then two rounded products and one rounded sum (<= 2^-24 relative
+        # each), so |error| <= 2^-22 * (|e| + |o|).
+        tol = 2.0 ** -22 * (np.abs(x[448::2]) + np.abs(x[449::2])).astype(np.float64)
+        assert (np.abs(y[448::2] - w.real) <= tol).all()
+        assert (np.abs(y[449::2] - w.imag) <= tol).all()
+
+
+def test_rope_inverse_after_forward_recovers_input():
+    cache = synth.cos_sin_cache(65536)
+    rng = np.random.default_rng(4)
+    for p in rng.integers(0, 65536, size=64):
+        x = _head(int(p), std=3.0)
+        back = oracle.rope_head(oracle.rope_head(x, cache[p], False), cache[p], True)
+        assert (np.abs(back - x) <= 1e-5 * np.maximum(1.0, np.abs(x))).all()
+
+
+def test_rope_pair_columns_are_distinct():
+    # Row with c_i = (i+1)/64 and s_i = (i+65)/128 (exact fp32 values): with
+    # e = 1, o = 0 the inverse gives e' = c_i, o' = -s_i for pair 224+i, which
+    # pins which column each pair reads.
+    i = np.arange(32)
+    row = np.concatenate([(i + 1) / 64.0, (i + 65) / 128.0]).astype(np.float32)
+    x = np.zeros(512, np.float32)
+    x[448::2] = 1.0
+    y = oracle.rope_head(x, row, inverse=True)
+    assert (y[448::2] == row[:32]).all() and (y[449::2] == -row[32:]).all()
+    y = oracle.rope_head(x, row, inverse=False)
+    assert (y[448::2] == row[:32]).all() and (y[449::2] == row[32:]).all()
+
+
+# ----------------------------------------------------------------- quant
+
+def _check_dequant_bound(x, codes, scales):
+    for b in range(4):
+        xb = x[128 * b:128 * (b + 1)].astype(np.float64)
+        s = float(scales[b])
+        deq = oracle.e4m3_to_f32(codes[128 * b:128 * (b + 1)]).astype(np.float64) * s
+        # code rounding: half an e4m3 ulp of x/s (in units of s); plus the two
+        # fp32 roundings of 1/s and x*(1/s): <= 2^-22 |x|
+        bound = 0.5 * e4m3_ulp(xb / s) * s + 2.0 ** -22 * np.abs(xb) + 1e-45
+        assert (np.abs(deq - xb) <= bound).all(), b
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_quant_fp32_scale_properties(seed):
+    x = _head(seed, std=2.0)
+    x[5] = 37.0  # an outlier in block 0
+    codes, sc, _ = oracle.quant_head(x, oracle.SCALE_FP32, 1e-10)
+    _check_dequant_bound(x, codes, sc)
+    for b in range(4):
+        blk = codes[128 * b:128 * (b + 1)]
+        dec = oracle.e4m3_to_f32(blk)
+        # the block's largest magnitude maps to exactly +-448 (code 0x7E/0xFE)
+        assert np.abs(dec).max() == 448.0
+        am = np.abs(x[128 * b:128 * (b + 1)]).max()
+        # scale is amax/448 up to one fp32 rounding
+        assert abs(float(sc[b]) - am / 448.0) <= 2.0 ** -24 * am / 448.0
+
+
+def test_quant_scale_is_exact_quotient():
+    x = _head(9)
+    codes, sc, _ = oracle.quant_head(x, oracle.SCALE_FP32, 1e-10)
+    am = np.abs(x.reshape(4, 128)).max(axis=1).astype(np.float32)
+    assert (f32_bits(sc) == f32_bits(am / np.float32(448.0))).all()
+
+
+def test_quant_blocks_are_independent():
+    x = _head(8)
+    for b in range(4):
+        x[128 * b:128 * (b + 1)] *= np.float32(10.0 ** b)
+    codes, sc, _ = oracle.quant_head(x, oracle.SCALE_FP32, 1e-10)
+    assert np.all(sc[1:] / sc[:-1] > 5)  # each scale follows its own block
+    _check_dequant_bound(x, codes, sc)
+
+
+@pytest.mark.parametrize("k", [0, -3, 5])
+def test_quant_power_of_two_scale_reduces_to_torch_cast(k):
+    # If a block's amax is 448 * 2^k the scale is exactly 2^k, 1/s is exact,
+    # and the codes are torch's e4m3 cast of x * 2^-k.
+    rng = np.random.default_rng(100 + k)
+    x = (rng.uniform(-1, 1, 512) * 448.0).astype(np.float32)
+    for b in range(4):
+        x[128 * b + 3] = 448.0
+    x = (x * np.float32(2.0 ** k)).astype(np.float32)
+    codes, sc, _ = oracle.quant_head(x, oracle.SCALE_FP32, 1e-10)
+    assert (sc == np.float32(2.0 ** k)).all()
+    assert (codes == torch_e4m3(x * np.float32(2.0 ** -k))).all()
+
+
+def test_quant_zero_block_uses_eps():
+    x = _head(12)
+    x[128:256] = 0.0
+    eps = 1e-10
+    codes, sc, _ = oracle.quant_head(x, oracle.SCALE_FP32, eps)
+    assert (codes[128:256] == 0).all()
+    assert abs(float(sc[1]) - eps / 448.0) <= 2.0 ** -23 * eps / 448.0
+    x[128:256] = -0.0
+    codes, _, _ = oracle.quant_head(x, oracle.SCALE_FP32, eps)
+    assert (codes[128:256] == 0x80).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quant_ue8m0_properties(seed):
+    x = _head(seed, std=3.0)
+    x[300] = -250.0
+    codes, sc, word = oracle.quant_head(x, oracle.SCALE_UE8M0, 1e-10)
+    for b in range(4):
+        am = float(np.abs(x[128 * b:128 * (b + 1)]).max())
+        t = np.float32(am) / np.float32(448.0)
+        s = float(sc[b])
+        m, e = np.frexp(s)
+        assert m == 0.5  # a power of two
+        assert s / 2 < t <= s
+        assert ((word >> (8 * b)) & 0xFF) == int(e - 1) + 127
+        dec = oracle.e4m3_to_f32(codes[128 * b:128 * (b + 1)]).astype(np.float64) * s
+        xb = x[128 * b:128 * (b + 1)].astype(np.float64)
+        # x * 2^-k is exact, so only the e4m3 rounding remains
+        assert (np.abs(dec - xb) <= 0.5 * e4m3_ulp(xb / s) * s + 1e-45).all()
+        # and the codes are torch's cast of the exactly scaled values
+        assert (codes[128 * b:128 * (b + 1)] ==
+                torch_e4m3(np.clip(x[128 * b:128 * (b + 1)] / np.float32(s), -448, 448))).all()
+
+
+# --------------------------------------------------------------- RMSNorm
+
+def _rms64(x, w, eps):
+    x = x.astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x) + eps)
+    return x * r * (1.0 if w is None else bf16_value(w).astype(np.float64))
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_rmsnorm_matches_fp64(eps):
+    w = synth.uniform_bf16((512,), 3, synth.T_W, 0.5, 1.5)
+    for seed in range(8):
+        x = _head(seed, std=2.0)
+        y = oracle.rmsnorm_head(x, w, eps).astype(np.float64)
+        ref = _rms64(x, w, eps)
+        assert (np.abs(y - ref) <= 4e-6 * np.abs(ref) + 1e-30).all()
+
+
+def test_rmsnorm_constant_row_closed_form():
+    for c in (0.5, 3.0, -7.25):
+        x = np.full(512, c, np.float32)
+        y = oracle.rmsnorm_head(x, None, 1e-6).astype(np.float64)
+        ref = c / np.sqrt(c * c + 1e-6)
+        assert (np.abs(y - ref) <= 2.0 ** -21 * abs(ref)).all()
+
+
+def test_rmsnorm_null_weight_equals_unit_weight():
+    x = _head(21)
+    ones = np.full(512, 0x3F80, np.uint16)  # bf16 1.0
+    a = oracle.rmsnorm_head(x, None, 1e-6)
+    b = oracle.rmsnorm_head(x, ones, 1e-6)
+    assert (f32_bits(a) == f32_bits(b)).all()
+
+
+def test_rmsnorm_sum_order_hand_derived():
+    # Chunk 0 = [2^12, 1 x 7]: left to right, 2^24 + 1 rounds back to 2^24
+    # (tie to even) seven times -> 2^24.  Chunks 2 and 3 each hold [1, 0 x 7].
+    # Butterfly k=1 gives chunk0+chunk1 = 2^24 and chunk2+chunk3 = 2; k=2 adds
+    # them: 2^24 + 2 exactly.  (Left-to-right over all 512 dims would give
+    # 2^24; summing chunk 0 right-to-left would give 2^24 + 8.)
+    x = np.zeros(512, np.float32)
+    x[0] = 2.0 ** 12
+    x[1:8] = 1.0
+    x[16] = 1.0
+    x[24] = 1.0
+    ss = np.float32(2.0 ** 24 + 2)
+    mean = ss * np.float32(1.0 / 512.0)
+    r = np.float32(1.0) / np.sqrt(mean + np.float32(1e-6), dtype=np.float32)
+    y = oracle.rmsnorm_head(x, None, 1e-6)
+    assert f32_bits(y[1]) == f32_bits(np.float32(1.0) * r)
+    ss_wrong = np.float32(2.0 ** 24)
+    r_wrong = np.float32(1.0) / np.sqrt(ss_wrong * np.float32(1 / 512) + np.float32(1e-6),
+                                        dtype=np.float32)
+    assert r != r_wrong  # the test can tell the orders apart
