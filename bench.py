@@ -1,0 +1,272 @@
+"""Benchmark of the fused RoPE + block-FP8 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only irq|qnr|kvi|decode|copy]
+
+A step is one launch of ``inv_rope_fp8_quant`` over the prefill workload
+(16384 tokens x 32 heads in 4 groups of 8, head dim 512, bf16 in, e4m3 +
+fp32 block-128 scales out; synthetic inputs already resident in HBM).  The
+timed region is K back-to-back launches on one stream, bracketed by HIP
+events recorded on that same stream and by device synchronizations.  The JSON
+line reports achieved HBM throughput over the algorithmic bytes, tokens/s,
+the roofline fraction against the 8 TB/s HBM3E peak, HBM traffic from
+rocprofv3 counters when they were taken on the current kernel source, and
+the CPU oracle timed on this host.  The other ops (qnorm_rope and
+kv_rope_quant_insert on the forward workload, and decode latencies) are timed
+the same way and reported under "extra".
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "irq_prefill_n16384_h32_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", "ropequant.hip")
+
+# Algorithmic bytes (what the op must move; caches assumed cold):
+#   inv_rope_fp8_quant per (token, head): 1024 B bf16 read + 512 B e4m3 write
+#     + 16 B fp32 scales (4 B in ue8m0); per token: 8 B position + 256 B cos/sin row.
+#   qnorm_rope per live head: 1024 B read + 1024 B write; per pad head 1024 B
+#     write; per token 8 + 256 B; plus the 1024 B weight once.
+#   kv_rope_quant_insert per token: 1024 B read + 528 B record + 8 B slot
+#     + 8 + 256 B.
+
+
+def irq_bytes(N, H, fmt="fp32"):
+    return N * H * (1024 + 512 + (16 if fmt == "fp32" else 4)) + N * (8 + 256)
+
+
+def qnr_bytes(N, Hq, Hpad):
+    return N * Hq * 2048 + N * (Hpad - Hq) * 1024 + N * 264 + 1024
+
+
+def kvi_bytes(N):
+    return N * (1024 + 528 + 8 + 264)
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per launch
+
+
+def to_dev(a, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def bench_irq(args, device, stream, fmt="fp32"):
+    import rope_fp8_quant_amd as rq
+    from rope_fp8_quant_amd import synth
+    cfg = synth.IRQ_PREFILL
+    t0 = time.time()
+    o, pos, cache = synth.irq_inputs(cfg)
+    print(f"[bench] irq inputs drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    N, H, hpg = cfg["N"], cfg["H"], cfg["hpg"]
+    od, pd, cd = to_dev(o, device), to_dev(pos, device), to_dev(cache, device)
+    out, sc = rq.empty_inv_rope_fp8_quant_outputs(N, H, hpg, device, fmt)
+
+    def step():
+        rq.inv_rope_fp8_quant(od, pd, cd, hpg, out, sc, fmt)
+
+    ms = time_launches(step, args.steps, args.warmup, stream)
+    return cfg, ms, (o, pos, cache)
+
+
+def bench_qnr_kvi(args, device, stream):
+    import torch
+
+    import rope_fp8_quant_amd as rq
+    from rope_fp8_quant_amd import synth
+    res = {}
+    if args.only in (None, "qnr"):
+        cfg = synth.QNR_FORWARD
+        q, w, pos, cache = synth.qnr_inputs(cfg)
+        qd, wd, pd, cd = (to_dev(x, device) for x in (q, w, pos, cache))
+        q_out = torch.empty((cfg["N"], cfg["Hpad"], 512), dtype=torch.bfloat16, device=device)
+        del q
+        ms = time_launches(lambda: rq.qnorm_rope(qd, wd, pd, cd, q_out, cfg["eps"]),
+                           args.steps, args.warmup, stream)
+        b = qnr_bytes(cfg["N"], cfg["Hq"], cfg["Hpad"])
+        res["qnorm_rope"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
+                                 gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+        del qd, q_out
+    if args.only in (None, "kvi"):
+        cfg = synth.KVI_FORWARD
+        kv, pos, slots, cache = synth.kvi_inputs(cfg)
+        kd, pd, sd, cd = (to_dev(x, device) for x in (kv, pos, slots, cache))
+        k_cache = rq.empty_kv_cache(cfg["num_blocks"], cfg["block_size"], device, fill=0xAA)
+        ms = time_launches(
+            lambda: rq.kv_rope_quant_insert(kd, pd, cd, sd, k_cache, cfg["block_size"]),
+            args.steps, args.warmup, stream)
+        b = kvi_bytes(cfg["N"])
+        res["kv_rope_quant_insert"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
+                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+    return res
+
+
+def bench_decode(args, device, stream):
+    import torch
+
+    import rope_fp8_quant_amd as rq
+    from rope_fp8_quant_amd import synth
+    res = {}
+    cache = to_dev(synth.cos_sin_cache(65536), device)
+    for N in synth.DECODE_NS:
+        cfg = dict(synth.IRQ_TINY, N=N, H=32, hpg=8, max_pos=65536, seed=40 + N)
+        o, pos, _ = synth.irq_inputs(cfg)
+        od, pd = to_dev(o, device), to_dev(pos, device)
+        out, sc = rq.empty_inv_rope_fp8_quant_outputs(N, 32, 8, device)
+        ms = time_launches(lambda: rq.inv_rope_fp8_quant(od, pd, cache, 8, out, sc),
+                           args.steps, args.warmup, stream)
+        q = to_dev(synth.normal_bf16((N, 32, 512), 50 + N, synth.T_Q), device)
+        q_out = torch.empty((N, 128, 512), dtype=torch.bfloat16, device=device)
+        msq = time_launches(lambda: rq.qnorm_rope(q, None, pd, cache, q_out, 1e-6),
+                            args.steps, args.warmup, stream)
+        res[f"N{N}"] = dict(irq_us=ms * 1e3, irq_gbs=irq_bytes(N, 32) / ms / 1e6,
+                            qnr_us=msq * 1e3, qnr_gbs=qnr_bytes(N, 32, 128) / msq / 1e6)
+    return res
+
+
+def bench_copy(args, device, stream):
+    """Plain 1 GiB device copy, the calibration kernel for HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    ms = time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+    return dict(bytes_read=n, bytes_written=n, us=ms * 1e3, gbs=2 * n / ms / 1e6)
+
+
+def cpu_baseline(irq_inputs, budget_s=12.0):
+    """The CPU oracle (single-threaded C) on this host, on a token prefix of
+    the prefill workload sized to about budget_s seconds of work."""
+    import oracle
+    o, pos, cache = irq_inputs
+    N, H = o.shape[0], o.shape[1]
+    n = 256
+    t = time.perf_counter()
+    oracle.inv_rope_fp8_quant(o[:n], pos[:n], cache, 8)
+    dt = time.perf_counter() - t
+    n2 = int(min(N, max(n, n * budget_s / max(dt, 1e-6))))
+    t = time.perf_counter()
+    oracle.inv_rope_fp8_quant(np.ascontiguousarray(o[:n2]), pos[:n2].copy(), cache, 8)
+    dt = time.perf_counter() - t
+    gbs = irq_bytes(n2, H) / dt / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
+                tokens_per_s=round(n2 / dt, 1),
+                sample=f"first {n2} of {N} tokens x {H} heads of the same workload, one "
+                       f"thread, {dt:.1f} s")
+
+
+def traffic_from_profile():
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "decode", "copy"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path has no cross-GPU step and this "
+              "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rope_fp8_quant_amd as rq
+    rq.abi_version()  # loads libropequant.so or raises
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    stream = torch.cuda.current_stream(device)
+
+    if args.only == "copy":
+        print(json.dumps({"copy_calibration": bench_copy(args, device, stream)}))
+        return
+    if args.only in ("qnr", "kvi"):
+        print(json.dumps({"extra": bench_qnr_kvi(args, device, stream)}))
+        return
+    if args.only == "decode":
+        print(json.dumps({"decode": bench_decode(args, device, stream)}))
+        return
+
+    cfg, ms, host_inputs = bench_irq(args, device, stream)
+    N, H = cfg["N"], cfg["H"]
+    b = irq_bytes(N, H)
+    gbs = b / ms / 1e6
+    extra = {}
+    if args.only is None:
+        torch.cuda.empty_cache()
+        _, ms_ue, _ = bench_irq(args, device, stream, "ue8m0")
+        extra["inv_rope_fp8_quant_ue8m0"] = dict(
+            us=ms_ue * 1e3, gbs=irq_bytes(N, H, "ue8m0") / ms_ue / 1e6)
+        torch.cuda.empty_cache()
+        extra.update(bench_qnr_kvi(args, device, stream))
+        torch.cuda.empty_cache()
+        extra["decode"] = bench_decode(args, device, stream)
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) + tokens/s, inv_rope_fp8_quant 16k tok x 32 heads",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded bf16 N(0,1) with 1% x20 outliers; positions 0..16383)",
+        "config": {"workload": cfg["name"], "n_tokens": N, "n_heads": H,
+                   "heads_per_group": cfg["hpg"], "head_dim": 512, "scale_fmt": "fp32",
+                   "algorithmic_bytes": b, "pages_convention_bytes": N * H * 1536},
+        "tokens_per_s": round(N / (ms / 1e3), 1),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(host_inputs)
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,6 +161,16 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
                          int32_t cache_block_size, int32_t scale_fmt, double eps,
                          void* stream);
 
+/*
+ * Launch-shape knob (process-wide, thread-safe): 0 lets the launch table pick
+ * the workgroup size from the unit count (256 threads for >= 16384 units,
+ * else 64, the analogue of [P4] section 4's program-count rule); 64, 128 or
+ * 256 forces that size for every later launch.  Results never depend on it;
+ * it exists for tuning and for the launch-invariance tests.  Returns RQ_OK
+ * or RQ_ERR_VALUE.
+ */
+int ropequant_set_block_threads(int threads);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* ropequant_strerror(int status);
 

@@ -1,1 +1,189 @@
-"""rope_fp8_quant_amd - placeholder; the binding is added with the HIP library."""
+"""Python binding of libropequant: fused RoPE + block-FP8 ops for MI355X.
+
+Thin argument marshalling only: each function checks the tensors the way the
+op's C++ entry checks them (dtype, device, shape, contiguity where required),
+then passes raw device pointers, strides and torch's current HIP stream to the
+C entry point of the same name.  Every step of the computation runs in the
+library's gfx950 kernels; there is no other path.  Outputs are preallocated by
+the caller and written in place (the ``_out`` convention); the ``empty_*``
+helpers allocate correctly shaped outputs.
+
+Sources: the op semantics follow the analyses of vLLM PR #63540
+("한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE + FP8 quant
+커널 3.5배 가속기", sections 1-3) for ``inv_rope_fp8_quant`` and of vLLM PR
+#49236 ("vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선",
+sections 1-2) for ``qnorm_rope`` and ``kv_rope_quant_insert``.
+"""
+import torch
+
+from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, lib
+
+__all__ = [
+    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
+    "empty_inv_rope_fp8_quant_outputs", "empty_kv_cache", "set_block_threads",
+    "abi_version", "RopeQuantError", "RECORD_BYTES", "SCALE_FMTS",
+]
+
+RECORD_BYTES = 528
+SCALE_FMTS = {"fp32": RQ_SCALE_FP32, "ue8m0": RQ_SCALE_UE8M0}
+_BYTE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+_WORD_DTYPES = (torch.int32, torch.uint32)
+
+
+def _fmt(scale_fmt):
+    if scale_fmt not in SCALE_FMTS:
+        raise ValueError(f"scale_fmt must be one of {sorted(SCALE_FMTS)}")
+    return SCALE_FMTS[scale_fmt]
+
+
+def _cuda(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _same_device(ref, *named):
+    for t, name in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device}")
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
+    if positions.dtype != torch.int64 or positions.dim() != 1 or positions.shape[0] != n_tokens:
+        raise ValueError("positions must be int64 [N]")
+    if not positions.is_contiguous():
+        raise ValueError("positions must be contiguous")
+    if (cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2
+            or cos_sin_cache.shape[1] != 64 or not cos_sin_cache.is_contiguous()):
+        raise ValueError("cos_sin_cache must be contiguous float32 [max_pos, 64]")
+
+
+def abi_version():
+    return lib().ropequant_abi_version()
+
+
+def set_block_threads(threads=0):
+    """Force the workgroup size (64, 128, 256) or restore the table (0)."""
+    check("ropequant_set_block_threads", lib().ropequant_set_block_threads(int(threads)))
+
+
+def empty_inv_rope_fp8_quant_outputs(n_tokens, n_heads, heads_per_group, device,
+                                     scale_fmt="fp32"):
+    """Group-major outputs: codes uint8 [G, N, hpg*512] and scales
+    float32 [G, N, hpg*4] (fp32) or int32 [G, N, hpg] (ue8m0 words)."""
+    G = n_heads // heads_per_group
+    out = torch.empty((G, n_tokens, heads_per_group * 512), dtype=torch.uint8, device=device)
+    if _fmt(scale_fmt) == RQ_SCALE_UE8M0:
+        sc = torch.empty((G, n_tokens, heads_per_group), dtype=torch.int32, device=device)
+    else:
+        sc = torch.empty((G, n_tokens, heads_per_group * 4), dtype=torch.float32, device=device)
+    return out, sc
+
+
+def empty_kv_cache(num_blocks, cache_block_size, device, fill=None):
+    """uint8 [num_blocks, cache_block_size * 528] paged cache."""
+    if fill is None:
+        return torch.empty((num_blocks, cache_block_size * RECORD_BYTES), dtype=torch.uint8,
+                           device=device)
+    return torch.full((num_blocks, cache_block_size * RECORD_BYTES), fill, dtype=torch.uint8,
+                      device=device)
+
+
+def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales,
+                       scale_fmt="fp32", eps=1e-10, stream=None):
+    """Inverse RoPE + block-128 e4m3 quantization of o [N, H, 512] bf16.
+
+    out: uint8 / float8_e4m3fn [G, N, hpg*512] (any strides on the first two
+    dims, last dim contiguous) - e.g. ``t.view(N, G, hpg*512).transpose(0, 1)``
+    of a token-major [N, H, 512] tensor.  scales: float32 [G, N, hpg*4] for
+    "fp32" or int32/uint32 [G, N, hpg] words for "ue8m0" (any strides).
+    """
+    fmt = _fmt(scale_fmt)
+    _cuda(o, "o")
+    if o.dtype != torch.bfloat16 or o.dim() != 3 or o.shape[2] != 512 or o.stride(2) != 1:
+        raise ValueError("o must be bf16 [N, H, 512] with a contiguous last dim")
+    N, H, _ = o.shape
+    hpg = int(heads_per_group)
+    if hpg < 1 or H % hpg:
+        raise ValueError("heads_per_group must divide the head count")
+    G = H // hpg
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if out.dtype not in _BYTE_DTYPES or tuple(out.shape) != (G, N, hpg * 512) or (
+            out.stride(2) != 1):
+        raise ValueError(f"out must be uint8/float8_e4m3fn [{G}, {N}, {hpg * 512}], last dim "
+                         "contiguous")
+    if fmt == RQ_SCALE_UE8M0:
+        if scales.dtype not in _WORD_DTYPES or tuple(scales.shape) != (G, N, hpg):
+            raise ValueError(f"ue8m0 scales must be int32/uint32 [{G}, {N}, {hpg}]")
+    elif scales.dtype != torch.float32 or tuple(scales.shape) != (G, N, hpg * 4):
+        raise ValueError(f"fp32 scales must be float32 [{G}, {N}, {hpg * 4}]")
+    _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"),
+                 (scales, "scales"))
+    rc = lib().inv_rope_fp8_quant(
+        o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0], N, H, hpg, fmt, float(eps),
+        out.data_ptr(), out.stride(0), out.stride(1),
+        scales.data_ptr(), scales.stride(0), scales.stride(1), scales.stride(2),
+        _stream(o.device, stream))
+    check("inv_rope_fp8_quant", rc)
+
+
+def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, stream=None):
+    """Per-head RMSNorm + forward RoPE of q_in [N, Hq, 512] bf16 into the
+    contiguous q_out [N, q_head_padded, 512] bf16; pad heads are zeroed.
+    norm_weight: bf16 [512] or None."""
+    _cuda(q_in, "q_in")
+    if q_in.dtype != torch.bfloat16 or q_in.dim() != 3 or q_in.shape[2] != 512 or (
+            q_in.stride(2) != 1):
+        raise ValueError("q_in must be bf16 [N, Hq, 512] with a contiguous last dim")
+    N, Hq, _ = q_in.shape
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if (q_out.dtype != q_in.dtype or q_out.dim() != 3 or q_out.shape[0] != N
+            or q_out.shape[2] != 512 or not q_out.is_contiguous()):
+        raise ValueError("q_out must be contiguous bf16 [N, q_head_padded, 512]")
+    if q_out.shape[1] < Hq:
+        raise ValueError("q_head_padded must be >= num_heads_q")
+    if norm_weight is not None and (norm_weight.dtype != torch.bfloat16
+                                    or tuple(norm_weight.shape) != (512,)
+                                    or not norm_weight.is_contiguous()):
+        raise ValueError("norm_weight must be contiguous bf16 [512] or None")
+    _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                 (q_out, "q_out"), (norm_weight, "norm_weight"))
+    rc = lib().qnorm_rope(
+        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
+        None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
+        cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, q_out.shape[1], float(eps),
+        q_out.data_ptr(), _stream(q_in.device, stream))
+    check("qnorm_rope", rc)
+
+
+def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size,
+                         scale_fmt="fp32", eps=1e-10, stream=None):
+    """Forward RoPE + block-128 e4m3 quantization of kv [N, 512] bf16, each
+    token's 528-byte record written at its slot of the paged uint8 cache
+    k_cache [num_blocks, block_bytes] (block stride = k_cache.stride(0))."""
+    fmt = _fmt(scale_fmt)
+    _cuda(kv, "kv")
+    if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != 512 or kv.stride(1) != 1:
+        raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
+    N = kv.shape[0]
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
+            or not slot_mapping.is_contiguous()):
+        raise ValueError("slot_mapping must be contiguous int64 [N]")
+    if k_cache.dtype != torch.uint8 or k_cache.dim() != 2 or k_cache.stride(1) != 1:
+        raise ValueError("k_cache must be uint8 [num_blocks, block_bytes]")
+    bs = int(cache_block_size)
+    if k_cache.shape[1] < bs * RECORD_BYTES:
+        raise ValueError("k_cache block_bytes must hold cache_block_size * 528 bytes")
+    _same_device(kv, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                 (slot_mapping, "slot_mapping"), (k_cache, "k_cache"))
+    rc = lib().kv_rope_quant_insert(
+        kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, k_cache.data_ptr(), k_cache.shape[0],
+        k_cache.stride(0), bs, fmt, float(eps), _stream(kv.device, stream))
+    check("kv_rope_quant_insert", rc)

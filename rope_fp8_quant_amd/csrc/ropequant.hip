@@ -1,0 +1,636 @@
+// libropequant: gfx950 kernels and the C ABI for the fused RoPE + block-FP8
+// steps around 512-dim attention heads.
+//
+// Sources (web pages; cited by title and section):
+//   [P1] "vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선"
+//        (analysis of vLLM PR #49236), section 1: the q-norm/RoPE + kv
+//        RoPE/quant/insert op, its caller-allocated q_out and its checks.
+//   [P3] "vLLM, DeepSeek V4 모델의 저지연을 위한 RMSNorm과 라우터 GEMV 연산
+//        융합으로 성능 극대화" (analysis of vLLM PR #41263), section 5: RMSNorm.
+//   [P4] "한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE +
+//        FP8 quant 커널 3.5배 가속기" (analysis of vLLM PR #63540): intro,
+//        sections 1-4 (heads per program, partner kept in registers, block
+//        amax, launch shape by program count).
+//
+// Work decomposition (all three kernels)
+//   A "unit" is one 512-dim head vector: (token, head) for inv_rope_fp8_quant
+//   and qnorm_rope, a token for kv_rope_quant_insert.  One unit is handled by
+//   one 16-lane DPP row of a wave64, so a wave holds 4 units and every
+//   cross-lane step stays inside a row.  Lane L of the row (quad q = L >> 2,
+//   r = L & 3) owns the four 8-dim chunks 16q + r + 4k (k = 0..3), i.e. dims
+//   [128q + 8r + 32k, +8): all 32 of its dims lie in quant block q, so a
+//   block's amax is a max over 32 registers and two quad DPP steps, and each
+//   lane divides once per block.  Every GPT-J pair (2i, 2i+1) sits in one
+//   lane as the low/high halves of a bf16 dword, so the RoPE partner never
+//   leaves its register ([P4] section 2's point, with no split/join at all).
+//   The rotated dims 448..511 are chunks k = 2, 3 of lanes 12..15.
+//   The pages group heads per program so that a program never straddles a
+//   wo_a group ([P4] section 1); here each row computes its own
+//   (group, head-in-group) address, so a wave may mix groups or tokens and
+//   ragged head counts need no special case.
+//
+// Arithmetic: IEEE binary32 basic operations, round to nearest even, no FMA
+// (built with -ffp-contract=off), correctly rounded divide and sqrt (the
+// compiler's default expansion), fp32 denormals preserved.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <atomic>
+
+#include "ropequant.h"
+
+namespace {
+
+constexpr int kHeadDim = 512;
+constexpr int kRecordBytes = 528;  // one paged-cache slot: 512 codes + 16 scale bytes
+constexpr float kE4m3Max = 448.0f;
+
+// ------------------------------------------------------------ small helpers
+
+// n / d for n < 2^31: q = (n * mul) >> shift with mul = ceil(2^(31+s) / d),
+// s = ceil(log2 d).  With e = mul*d - 2^(31+s) < d the error term n*e/(d*2^(31+s))
+// stays below 2^-s <= 1/d, so the floor is exact.
+struct Magic {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+__device__ __forceinline__ uint32_t magic_div(uint32_t n, Magic m) {
+  return (uint32_t)(((uint64_t)n * m.mul) >> m.shift);
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so each XCD
+// sees one contiguous range of units: a token's heads (and its cos/sin row)
+// then stay in one XCD's L2.  A bijection on [0, gridDim.x).
+__device__ __forceinline__ uint32_t xcd_block_id() {
+  const uint32_t nb = gridDim.x, b = blockIdx.x;
+  const uint32_t xcd = b & 7u, local = b >> 3;
+  const uint32_t q = nb >> 3, r = nb & 7u;
+  return (xcd < r) ? xcd * (q + 1u) + local : r * (q + 1u) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(__bf16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float bf_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(__bf16, (uint16_t)(w >> 16));
+}
+
+// DPP controls (row = 16 lanes)
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within the row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// The lane's 32 values: x[k][e] is dim lane_dim0 + 32k + e.
+struct Vals {
+  float x[4][8];
+};
+
+__device__ __forceinline__ int lane_dim0(int L) { return 128 * (L >> 2) + 8 * (L & 3); }
+
+__device__ __forceinline__ void unpack_bf16(const uint4 (&w)[4], Vals& v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t d[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v.x[k][2 * i] = bf_lo(d[i]);
+      v.x[k][2 * i + 1] = bf_hi(d[i]);
+    }
+  }
+}
+
+// cos/sin for the lane's rotated pairs (lanes 12..15 only): cs[0] = cos of
+// pairs in chunk k=2, cs[1] = cos for k=3, cs[2], cs[3] = the matching sin.
+struct RopeCS {
+  float4 c[2];
+  float4 s[2];
+};
+
+__device__ __forceinline__ void load_cs(const float* row, int r, RopeCS& cs) {
+  const float4* p = reinterpret_cast<const float4*>(row);
+  cs.c[0] = p[r];       // cos[4r .. 4r+3]
+  cs.c[1] = p[4 + r];   // cos[16+4r ..]
+  cs.s[0] = p[8 + r];   // sin[4r ..]      (column 32 + ...)
+  cs.s[1] = p[12 + r];  // sin[16+4r ..]
+}
+
+// GPT-J rotation of the lane's chunks 2 and 3 (dims 448..511 on lanes 12..15).
+//   INVERSE: e' = e*c + o*s,  o' = o*c - e*s   ([P4] section 2)
+//   forward: e' = e*c - o*s,  o' = o*c + e*s
+template <bool INVERSE>
+__device__ __forceinline__ void rope_lane(Vals& v, const RopeCS& cs) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const float cv[4] = {cs.c[kk].x, cs.c[kk].y, cs.c[kk].z, cs.c[kk].w};
+    const float sv[4] = {cs.s[kk].x, cs.s[kk].y, cs.s[kk].z, cs.s[kk].w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float e = v.x[2 + kk][2 * p], o = v.x[2 + kk][2 * p + 1];
+      const float ec = e * cv[p], os = o * sv[p], oc = o * cv[p], es = e * sv[p];
+      if (INVERSE) {
+        v.x[2 + kk][2 * p] = ec + os;
+        v.x[2 + kk][2 * p + 1] = oc - es;
+      } else {
+        v.x[2 + kk][2 * p] = ec - os;
+        v.x[2 + kk][2 * p + 1] = oc + es;
+      }
+    }
+  }
+}
+
+// Block quantization of the lane's 32 values ([P4] section 3).  The 4 lanes
+// of a quad share block q.  Returns the block's scale value (FP32 mode:
+// m/448; UE8M0: 2^k) and the exponent byte k+127 (UE8M0), and the codes as
+// 8 dwords (chunk k -> codes[2k], codes[2k+1]).
+template <int FMT>
+__device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& scale,
+                                              uint32_t& ebyte, uint32_t (&codes)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v.x[k][e]));
+  m = __builtin_fmaxf(m, dpp_f32<kQuadSwap1>(m));
+  m = __builtin_fmaxf(m, dpp_f32<kQuadSwap2>(m));
+  m = __builtin_fmaxf(m, eps);
+  float mult;
+  if (FMT == RQ_SCALE_UE8M0) {
+    const float t = m / kE4m3Max;
+    const uint32_t u = __builtin_bit_cast(uint32_t, t);
+    const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
+    scale = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
+    mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
+    ebyte = (uint32_t)(kexp + 127);
+  } else {
+    scale = m / kE4m3Max;
+    mult = 1.0f / scale;
+    ebyte = 0;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        q[e] = __builtin_amdgcn_fmed3f(v.x[k][4 * h + e] * mult, -kE4m3Max, kE4m3Max);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+      codes[2 * k + h] = (uint32_t)w;
+    }
+  }
+}
+
+// OR of the four blocks' exponent bytes into one word (block q in byte q).
+// Within a quad the byte is uniform, so the two mirrors act as xor-4 / xor-8.
+__device__ __forceinline__ uint32_t pack_ue8m0(uint32_t ebyte, int q) {
+  uint32_t w = ebyte << (8 * q);
+  w |= dpp_u32<kRowHalfMirror>(w);
+  w |= dpp_u32<kRowMirror>(w);
+  return w;
+}
+
+// --------------------------------------------------------------- kernels
+
+struct IrqParams {
+  const uint16_t* o;
+  int64_t o_st, o_sh;
+  const int64_t* positions;
+  const float* cs;
+  int64_t max_pos;
+  uint32_t units;  // n_tokens * n_heads
+  Magic div_heads, div_hpg;
+  uint32_t n_heads, hpg;
+  float eps;
+  uint8_t* out;
+  int64_t out_sg, out_st;
+  void* scales;
+  int64_t sc_sg, sc_st, sc_sb;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
+  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
+  const uint32_t unit = tid >> 4;
+  const int L = threadIdx.x & 15;
+  if (unit >= p.units) return;  // whole rows only: DPP never reads a retired lane
+  const uint32_t t = magic_div(unit, p.div_heads);
+  const uint32_t h = unit - t * p.n_heads;
+  const uint32_t g = magic_div(h, p.div_hpg);
+  const uint32_t j = h - g * p.hpg;
+  const int d0 = lane_dim0(L);
+
+  const int64_t pos = p.positions[t];
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  const uint4* src = reinterpret_cast<const uint4*>(p.o + (int64_t)t * p.o_st +
+                                                    (int64_t)h * p.o_sh + d0);
+  uint4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
+  RopeCS cs;
+  const bool rope = L >= 12;
+  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+
+  Vals v;
+  unpack_bf16(w, v);
+  if (rope) rope_lane<true>(v, cs);
+
+  float scale;
+  uint32_t ebyte, codes[8];
+  quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
+  const int q = L >> 2;
+  uint32_t word = 0;
+  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, q);
+  if (bad) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
+    scale = __builtin_nanf("");
+    word = 0xFFFFFFFFu;
+  }
+
+  uint8_t* dst = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim + d0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<uint2*>(dst + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
+  if (FMT == RQ_SCALE_UE8M0) {
+    if (L == 0)
+      static_cast<uint32_t*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                                       (int64_t)j * p.sc_sb] = word;
+  } else {
+    if ((L & 3) == 0)
+      static_cast<float*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                                    (int64_t)(j * 4 + q) * p.sc_sb] = scale;
+  }
+}
+
+struct QnrParams {
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  const uint16_t* weight;
+  const int64_t* positions;
+  const float* cs;
+  int64_t max_pos;
+  uint32_t units;  // n_tokens * q_head_padded
+  Magic div_hpad;
+  uint32_t hq, hpad;
+  float eps;
+  uint16_t* q_out;
+};
+
+template <bool HAS_WEIGHT>
+__global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
+  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
+  const uint32_t unit = tid >> 4;
+  const int L = threadIdx.x & 15;
+  if (unit >= p.units) return;
+  const uint32_t t = magic_div(unit, p.div_hpad);
+  const uint32_t h = unit - t * p.hpad;
+  const int d0 = lane_dim0(L);
+  uint4* dst = reinterpret_cast<uint4*>(p.q_out + (int64_t)unit * kHeadDim + d0);
+
+  if (h >= p.hq) {  // pad head: exact +0 ([P1] section 1)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[4 * k] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+
+  const int64_t pos = p.positions[t];
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  const uint4* src = reinterpret_cast<const uint4*>(p.q + (int64_t)t * p.q_st +
+                                                    (int64_t)h * p.q_sh + d0);
+  uint4 w[4], wt[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
+  if (HAS_WEIGHT) {
+    const uint4* wp = reinterpret_cast<const uint4*>(p.weight + d0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wt[k] = wp[4 * k];
+  }
+  RopeCS cs;
+  const bool rope = L >= 12;
+  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+
+  Vals v;
+  unpack_bf16(w, v);
+
+  // Sum of squares in the fixed tree: chunk sums left to right, then
+  // butterflies over the chunk index c = 16q + 4k + r for bit 0, 1 (lanes
+  // r^1, r^2), bit 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads q^1, q^2).
+  float ps[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float acc = v.x[k][0] * v.x[k][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
+    ps[k] = acc;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap2>(ps[k]);
+  float ss = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  ss = ss + dpp_f32<kRowHalfMirror>(ss);
+  ss = ss + dpp_f32<kRowMirror>(ss);
+  const float mean = ss * (1.0f / 512.0f);
+  const float r = 1.0f / sqrtf(mean + p.eps);
+
+  if (HAS_WEIGHT) {
+    Vals wv;
+    unpack_bf16(wt, wv);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * r) * wv.x[k][e];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * r;
+  }
+  if (rope) rope_lane<false>(v, cs);
+
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 f = {v.x[k][2 * i], v.x[k][2 * i + 1]};
+      o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    uint4 outv = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    if (bad) outv = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    dst[4 * k] = outv;
+  }
+}
+
+struct KviParams {
+  const uint16_t* kv;
+  int64_t kv_st;
+  const int64_t* positions;
+  const float* cs;
+  int64_t max_pos;
+  const int64_t* slots;
+  uint32_t n_tokens;
+  int64_t num_slots;
+  Magic div_bs;
+  uint32_t bs;
+  uint8_t* cache;
+  int64_t block_stride;
+  float eps;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
+  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
+  const uint32_t t = tid >> 4;
+  const int L = threadIdx.x & 15;
+  if (t >= p.n_tokens) return;
+  const int64_t slot = p.slots[t];
+  if (slot < 0 || slot >= p.num_slots) return;  // padding token, or no such slot
+  const int d0 = lane_dim0(L);
+
+  const int64_t pos = p.positions[t];
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  const uint4* src = reinterpret_cast<const uint4*>(p.kv + (int64_t)t * p.kv_st + d0);
+  uint4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
+  RopeCS cs;
+  const bool rope = L >= 12;
+  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+
+  Vals v;
+  unpack_bf16(w, v);
+  if (rope) rope_lane<false>(v, cs);
+
+  float scale;
+  uint32_t ebyte, codes[8];
+  quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
+  const int q = L >> 2;
+  uint32_t word = 0;
+  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, q);
+  if (bad) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
+    scale = __builtin_nanf("");
+    word = 0xFFFFFFFFu;
+  }
+
+  const uint32_t s32 = (uint32_t)slot;
+  const uint32_t blk = magic_div(s32, p.div_bs);
+  const uint32_t idx = s32 - blk * p.bs;
+  uint8_t* rec = p.cache + (int64_t)blk * p.block_stride + (int64_t)idx * kRecordBytes;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
+  if ((L & 3) == 0) {
+    uint32_t tail;
+    if (FMT == RQ_SCALE_UE8M0) tail = (q == 0) ? word : 0u;
+    else tail = __builtin_bit_cast(uint32_t, scale);
+    *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * q) = tail;
+  }
+}
+
+// ------------------------------------------------------------ host side
+
+std::atomic<int> g_block_threads{0};  // 0: launch table decides
+
+Magic make_magic(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << (31 + s)) + d - 1) / d;
+  return Magic{(uint32_t)m, 31u + s};
+}
+
+// Launch table: the analogue of [P4] section 4's program-count rule.  Many
+// units (prefill): 256-thread workgroups (16 units), plenty of them per CU.
+// Few units (decode): 64-thread workgroups (4 units) so the work spreads over
+// as many CUs as possible.  Results do not depend on the choice.
+int pick_block_threads(uint32_t units) {
+  const int forced = g_block_threads.load(std::memory_order_relaxed);
+  if (forced) return forced;
+  return units >= 16384u ? 256 : 64;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool eps_quant_ok(double eps) {
+  // finite and at least 2^-116 as fp32, so eps/448 stays normal and 1/s finite
+  if (!(eps == eps) || eps > 3.0e38 || eps < 0) return false;
+  const float e = (float)eps;
+  return e >= 0x1p-116f;
+}
+
+// Non-overlap of an index space sum_i n_i * s_i (+ row of `row` contiguous
+// elements): with dims of extent > 1 sorted by stride, each stride must exceed
+// the span of all inner dims.  Sufficient (not necessary) for disjointness.
+bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
+  int64_t ns[4], ss[4];
+  int m = 0;
+  for (int i = 0; i < nd; ++i)
+    if (n[i] > 1) { ns[m] = n[i]; ss[m] = s[i]; ++m; }
+  for (int i = 1; i < m; ++i)  // insertion sort by stride
+    for (int k = i; k > 0 && ss[k] < ss[k - 1]; --k) {
+      int64_t tn = ns[k]; ns[k] = ns[k - 1]; ns[k - 1] = tn;
+      int64_t ts = ss[k]; ss[k] = ss[k - 1]; ss[k - 1] = ts;
+    }
+  int64_t span = row;  // elements covered by the inner dims so far
+  for (int i = 0; i < m; ++i) {
+    if (ss[i] < span) return false;
+    span = (ns[i] - 1) * ss[i] + span;
+  }
+  return true;
+}
+
+int launch(const void* fn, uint32_t units, void* params, hipStream_t stream) {
+  const int threads = pick_block_threads(units);
+  const uint32_t per_block = (uint32_t)threads / 16u;
+  const uint32_t blocks = (units + per_block - 1) / per_block;
+  void* args[] = {params};
+  const hipError_t e =
+      hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, 0, stream);
+  return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ropequant_abi_version(void) { return ROPEQUANT_ABI_VERSION; }
+
+const char* ropequant_strerror(int status) {
+  switch (status) {
+    case RQ_OK: return "ok";
+    case RQ_ERR_NULL: return "a required pointer is NULL";
+    case RQ_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case RQ_ERR_STRIDE: return "a stride is non-positive or lets outputs overlap";
+    case RQ_ERR_ALIGN: return "a pointer or stride breaks the required alignment";
+    case RQ_ERR_VALUE: return "a scalar argument (scale_fmt, eps) is invalid";
+    case RQ_ERR_HIP: return "the HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}
+
+int ropequant_set_block_threads(int threads) {
+  if (threads != 0 && threads != 64 && threads != 128 && threads != 256) return RQ_ERR_VALUE;
+  g_block_threads.store(threads, std::memory_order_relaxed);
+  return RQ_OK;
+}
+
+int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
+                       const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                       int64_t n_tokens, int32_t n_heads, int32_t heads_per_group,
+                       int32_t scale_fmt, double eps, uint8_t* out, int64_t out_stride_group,
+                       int64_t out_stride_token, void* scales, int64_t sc_stride_group,
+                       int64_t sc_stride_token, int64_t sc_stride_block, void* stream) {
+  if (n_tokens < 0 || n_heads < 1 || heads_per_group < 1 || max_pos < 1) return RQ_ERR_SHAPE;
+  if (n_heads % heads_per_group) return RQ_ERR_SHAPE;
+  if ((int64_t)n_tokens * n_heads >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
+  if (scale_fmt != RQ_SCALE_FP32 && scale_fmt != RQ_SCALE_UE8M0) return RQ_ERR_VALUE;
+  if (!eps_quant_ok(eps)) return RQ_ERR_VALUE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!o || !positions || !cos_sin_cache || !out || !scales) return RQ_ERR_NULL;
+  if (o_stride_token < 1 || o_stride_head < 1 || out_stride_group < 1 || out_stride_token < 1 ||
+      sc_stride_group < 1 || sc_stride_token < 1 || sc_stride_block < 1)
+    return RQ_ERR_STRIDE;
+  if (!aligned(o, 16) || (o_stride_token % 8) || (o_stride_head % 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin_cache, 16) || !aligned(out, 16) || (out_stride_group % 16) ||
+      (out_stride_token % 16) || !aligned(scales, 4))
+    return RQ_ERR_ALIGN;
+  const int64_t G = n_heads / heads_per_group;
+  {
+    const int64_t n[2] = {G, n_tokens}, s[2] = {out_stride_group, out_stride_token};
+    if (!no_overlap(2, n, s, (int64_t)heads_per_group * kHeadDim)) return RQ_ERR_STRIDE;
+  }
+  {
+    const int64_t per = scale_fmt == RQ_SCALE_FP32 ? (int64_t)heads_per_group * 4 : heads_per_group;
+    const int64_t n[3] = {G, n_tokens, per}, s[3] = {sc_stride_group, sc_stride_token, sc_stride_block};
+    if (!no_overlap(3, n, s, 1)) return RQ_ERR_STRIDE;
+  }
+  IrqParams p;
+  p.o = o; p.o_st = o_stride_token; p.o_sh = o_stride_head;
+  p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
+  p.units = (uint32_t)(n_tokens * n_heads);
+  p.div_heads = make_magic((uint32_t)n_heads);
+  p.div_hpg = make_magic((uint32_t)heads_per_group);
+  p.n_heads = (uint32_t)n_heads; p.hpg = (uint32_t)heads_per_group;
+  p.eps = (float)eps;
+  p.out = out; p.out_sg = out_stride_group; p.out_st = out_stride_token;
+  p.scales = scales; p.sc_sg = sc_stride_group; p.sc_st = sc_stride_token; p.sc_sb = sc_stride_block;
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
+                                               : (const void*)irq_kernel<RQ_SCALE_FP32>;
+  return launch(fn, p.units, &p, (hipStream_t)stream);
+}
+
+int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+               const uint16_t* norm_weight, const int64_t* positions,
+               const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+               int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
+               void* stream) {
+  if (n_tokens < 0 || n_heads_q < 1 || max_pos < 1) return RQ_ERR_SHAPE;
+  if (q_head_padded < n_heads_q) return RQ_ERR_SHAPE;  // [P1] section 1 check
+  if ((int64_t)n_tokens * q_head_padded >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
+  if (!(eps > 0.0) || !((float)eps > 0.0f) || !((float)eps <= 3.0e38f)) return RQ_ERR_VALUE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!q_in || !positions || !cos_sin_cache || !q_out) return RQ_ERR_NULL;
+  if (q_stride_token < 1 || q_stride_head < 1) return RQ_ERR_STRIDE;
+  if (!aligned(q_in, 16) || (q_stride_token % 8) || (q_stride_head % 8) ||
+      !aligned(positions, 8) || !aligned(cos_sin_cache, 16) || !aligned(q_out, 16) ||
+      (norm_weight && !aligned(norm_weight, 16)))
+    return RQ_ERR_ALIGN;
+  QnrParams p;
+  p.q = q_in; p.q_st = q_stride_token; p.q_sh = q_stride_head;
+  p.weight = norm_weight; p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
+  p.units = (uint32_t)(n_tokens * q_head_padded);
+  p.div_hpad = make_magic((uint32_t)q_head_padded);
+  p.hq = (uint32_t)n_heads_q; p.hpad = (uint32_t)q_head_padded;
+  p.eps = (float)eps; p.q_out = q_out;
+  const void* fn = norm_weight ? (const void*)qnr_kernel<true> : (const void*)qnr_kernel<false>;
+  return launch(fn, p.units, &p, (hipStream_t)stream);
+}
+
+int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
+                         const float* cos_sin_cache, int64_t max_pos,
+                         const int64_t* slot_mapping, int64_t n_tokens, uint8_t* k_cache,
+                         int64_t num_blocks, int64_t block_stride_bytes,
+                         int32_t cache_block_size, int32_t scale_fmt, double eps,
+                         void* stream) {
+  if (n_tokens < 0 || max_pos < 1 || num_blocks < 1 || cache_block_size < 1) return RQ_ERR_SHAPE;
+  if (n_tokens >= (int64_t(1) << 27)) return RQ_ERR_SHAPE;
+  if (num_blocks * (int64_t)cache_block_size >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
+  if (block_stride_bytes < (int64_t)cache_block_size * kRecordBytes) return RQ_ERR_STRIDE;
+  if (scale_fmt != RQ_SCALE_FP32 && scale_fmt != RQ_SCALE_UE8M0) return RQ_ERR_VALUE;
+  if (!eps_quant_ok(eps)) return RQ_ERR_VALUE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!kv || !positions || !cos_sin_cache || !slot_mapping || !k_cache) return RQ_ERR_NULL;
+  if (kv_stride_token < 1) return RQ_ERR_STRIDE;
+  if (!aligned(kv, 16) || (kv_stride_token % 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin_cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
+      (block_stride_bytes % 16))
+    return RQ_ERR_ALIGN;
+  KviParams p;
+  p.kv = kv; p.kv_st = kv_stride_token; p.positions = positions; p.cs = cos_sin_cache;
+  p.max_pos = max_pos; p.slots = slot_mapping; p.n_tokens = (uint32_t)n_tokens;
+  p.num_slots = num_blocks * (int64_t)cache_block_size;
+  p.div_bs = make_magic((uint32_t)cache_block_size); p.bs = (uint32_t)cache_block_size;
+  p.cache = k_cache; p.block_stride = block_stride_bytes; p.eps = (float)eps;
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
+                                               : (const void*)kvi_kernel<RQ_SCALE_FP32>;
+  return launch(fn, p.n_tokens, &p, (hipStream_t)stream);
+}
+
+}  // extern "C"

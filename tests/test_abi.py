@@ -1,0 +1,170 @@
+"""The C ABI on the host: exported symbols, status codes, argument validation.
+
+No kernel runs here.  The validation cases pass fake (never dereferenced)
+device addresses, so they are skipped where a GPU is visible: a validation
+bug there would launch a kernel on them.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from rope_fp8_quant_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ropequant.h")
+
+OK, NULL, SHAPE, STRIDE, ALIGN, VALUE = 0, -1, -2, -3, -4, -5
+
+host_only = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="passes fake device pointers; host-only check")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert"}
+    syms = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    L = _lib.lib()
+    for n in names:
+        getattr(L, n)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+ROPEQUANT_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert _lib.lib().ropequant_abi_version() == int(m.group(1))
+
+
+def test_status_strings_distinct():
+    L = _lib.lib()
+    msgs = [L.ropequant_strerror(s).decode() for s in range(0, -7, -1)]
+    assert len(set(msgs)) == 7 and all(msgs)
+    assert L.ropequant_strerror(-99).decode() == "unknown status"
+
+
+def test_block_threads_knob():
+    L = _lib.lib()
+    assert L.ropequant_set_block_threads(100) == VALUE
+    for t in (64, 128, 256, 0):
+        assert L.ropequant_set_block_threads(t) == OK
+
+
+A = 0x100000  # fake, 256-byte aligned "device" addresses
+
+
+def irq(**kw):
+    a = dict(o=A, ost=32 * 512, osh=512, pos=A, cs=A, max_pos=4096, n=16, h=32, hpg=8, fmt=0,
+             eps=1e-10, out=A, osg=16 * 8 * 512, ost2=8 * 512, sc=A, ssg=16 * 32, sst=32, ssb=1)
+    a.update(kw)
+    return _lib.lib().inv_rope_fp8_quant(
+        a["o"], a["ost"], a["osh"], a["pos"], a["cs"], a["max_pos"], a["n"], a["h"], a["hpg"],
+        a["fmt"], a["eps"], a["out"], a["osg"], a["ost2"], a["sc"], a["ssg"], a["sst"],
+        a["ssb"], None)
+
+
+def qnr(**kw):
+    a = dict(q=A, qst=64 * 512, qsh=512, w=A, pos=A, cs=A, max_pos=8192, n=8, hq=64, hpad=128,
+             eps=1e-6, out=A)
+    a.update(kw)
+    return _lib.lib().qnorm_rope(a["q"], a["qst"], a["qsh"], a["w"], a["pos"], a["cs"],
+                                 a["max_pos"], a["n"], a["hq"], a["hpad"], a["eps"], a["out"],
+                                 None)
+
+
+def kvi(**kw):
+    a = dict(kv=A, kst=512, pos=A, cs=A, max_pos=8192, slots=A, n=8, cache=A, nb=256,
+             stride=64 * 528, bs=64, fmt=0, eps=1e-10)
+    a.update(kw)
+    return _lib.lib().kv_rope_quant_insert(a["kv"], a["kst"], a["pos"], a["cs"], a["max_pos"],
+                                           a["slots"], a["n"], a["cache"], a["nb"], a["stride"],
+                                           a["bs"], a["fmt"], a["eps"], None)
+
+
+def test_zero_tokens_is_ok_without_pointers():
+    assert irq(n=0, o=None, pos=None, cs=None, out=None, sc=None) == OK
+    assert qnr(n=0, q=None, w=None, pos=None, cs=None, out=None) == OK
+    assert kvi(n=0, kv=None, pos=None, cs=None, slots=None, cache=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpg=7), SHAPE), (dict(n=-1), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(h=0), SHAPE), (dict(n=1 << 26, h=32), SHAPE),
+    (dict(fmt=2), VALUE), (dict(eps=0.0), VALUE), (dict(eps=float("nan")), VALUE),
+    (dict(eps=1e-40), VALUE), (dict(eps=float("inf")), VALUE),
+    (dict(o=None), NULL), (dict(pos=None), NULL), (dict(cs=None), NULL),
+    (dict(out=None), NULL), (dict(sc=None), NULL),
+    (dict(ost=0), STRIDE), (dict(ssb=0), STRIDE),
+    (dict(o=A + 8), ALIGN), (dict(osh=516), ALIGN), (dict(ost=32 * 512 + 4), ALIGN),
+    (dict(cs=A + 4), ALIGN), (dict(pos=A + 4), ALIGN), (dict(out=A + 8), ALIGN),
+    (dict(ost2=8 * 512 + 8), ALIGN), (dict(sc=A + 2), ALIGN),
+    (dict(ost2=4 * 512), STRIDE),                 # token rows overlap (hpg*512 bytes each)
+    (dict(osg=8 * 512, ost2=16 * 512), STRIDE),   # group rows collide with token rows
+    (dict(sst=16), STRIDE),                       # scale rows overlap
+])
+def test_irq_validation(kw, status):
+    assert irq(**kw) == status
+
+
+@host_only
+def test_irq_token_major_strides_are_accepted_by_validation():
+    # [N, H, 512] token-major strides pass validation; with no GPU the launch
+    # itself is refused by the runtime, which must come back as RQ_ERR_HIP.
+    assert irq(osg=8 * 512, ost2=32 * 512, ssg=32, sst=128, ssb=1) == -6
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpad=63), SHAPE), (dict(hq=0), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(n=1 << 25, hpad=128), SHAPE),
+    (dict(eps=0.0), VALUE), (dict(eps=-1.0), VALUE), (dict(eps=1e-50), VALUE),
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(pos=None), NULL), (dict(cs=None), NULL),
+    (dict(qst=0), STRIDE),
+    (dict(q=A + 2), ALIGN), (dict(qsh=500), ALIGN), (dict(w=A + 8), ALIGN),
+    (dict(out=A + 4), ALIGN), (dict(cs=A + 8), ALIGN),
+])
+def test_qnr_validation(kw, status):
+    assert qnr(**kw) == status
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=0), SHAPE), (dict(nb=0), SHAPE), (dict(n=-3), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(nb=1 << 26, bs=64), SHAPE),
+    (dict(stride=64 * 528 - 16), STRIDE), (dict(kst=0), STRIDE),
+    (dict(fmt=5), VALUE), (dict(eps=0.0), VALUE),
+    (dict(kv=None), NULL), (dict(slots=None), NULL), (dict(cache=None), NULL),
+    (dict(stride=64 * 528 + 8), ALIGN), (dict(cache=A + 8), ALIGN), (dict(kv=A + 8), ALIGN),
+    (dict(kst=516), ALIGN), (dict(slots=A + 4), ALIGN),
+])
+def test_kvi_validation(kw, status):
+    assert kvi(**kw) == status
+
+
+def test_python_binding_rejects_host_tensors():
+    import rope_fp8_quant_amd as rq
+    o = torch.zeros((2, 8, 512), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rq.inv_rope_fp8_quant(o, torch.zeros(2, dtype=torch.int64), torch.zeros(4, 64), 8,
+                              torch.empty(1, 2, 4096, dtype=torch.uint8),
+                              torch.empty(1, 2, 32))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

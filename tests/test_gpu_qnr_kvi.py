@@ -1,0 +1,173 @@
+"""GPU parity of qnorm_rope and kv_rope_quant_insert (HIP path through the C
+ABI) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_fp8_quant_amd as rq
+from rope_fp8_quant_amd import synth
+from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
+
+
+@pytest.fixture(autouse=True)
+def _table_launch():
+    rq.set_block_threads(0)
+    yield
+    rq.set_block_threads(0)
+
+
+# ------------------------------------------------------------- qnorm_rope
+
+def qnr_gpu(q, w, pos, cache, hpad, eps, q_dev=None):
+    N = q.shape[0]
+    q_out = torch.empty((N, hpad, 512), dtype=torch.bfloat16, device=DEV)
+    q_out.view(torch.int16).fill_(-1)  # 0xFFFF everywhere: pads must be rewritten
+    rq.qnorm_rope(dev(q) if q_dev is None else q_dev, None if w is None else dev(w), dev(pos),
+                  dev(cache), q_out, eps)
+    torch.cuda.synchronize()
+    return host(q_out)
+
+
+def qnr_check(q, w, pos, cache, hpad, eps, what, q_dev=None):
+    print(f"[case] qnr {what} N={q.shape[0]} Hq={q.shape[1]} Hpad={hpad}", flush=True)
+    got = qnr_gpu(q, w, pos, cache, hpad, eps, q_dev)
+    exp = oracle.qnorm_rope(q, w, pos, cache, hpad, eps)
+    assert (got[:, q.shape[1]:] == 0).all(), "pad heads not zero"
+    assert_bits_equal(got, exp, f"qnr {what}")
+    return got
+
+
+def test_qnr_forward_full_size():
+    cfg = synth.QNR_FORWARD
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    qnr_check(q, w, pos, cache, cfg["Hpad"], cfg["eps"], "forward 8192x64->128")
+
+
+@pytest.mark.parametrize("threads", [64, 256])
+def test_qnr_ragged_no_weight(threads):
+    rq.set_block_threads(threads)
+    cfg = dict(synth.QNR_FORWARD, N=37, Hq=5, Hpad=7, max_pos=65536, seed=31)
+    q, _, pos, cache = synth.qnr_inputs(cfg)
+    qnr_check(q, None, pos, cache, 7, 1e-6, f"ragged no-weight threads={threads}")
+
+
+@pytest.mark.parametrize("N", synth.DECODE_NS)
+def test_qnr_decode_sizes(N):
+    cfg = dict(synth.QNR_FORWARD, N=N, Hq=32, Hpad=128, std=1.0, seed=50 + N)
+    q, w, _, cache = synth.qnr_inputs(cfg)
+    pos = synth.uniform_positions(N, 65536, 50 + N)
+    qnr_check(q, w, pos, synth.cos_sin_cache(65536), 128, 1e-6, "decode")
+
+
+def test_qnr_strided_input():
+    cfg = dict(synth.QNR_FORWARD, N=21, Hq=12, Hpad=16, seed=32)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    big = torch.zeros((21, 12, 1536), dtype=torch.bfloat16, device=DEV)
+    big[:, :, 1024:] = dev(q)
+    qnr_check(q, w, pos, cache, 16, 1e-6, "strided", q_dev=big[:, :, 1024:])
+
+
+def test_qnr_degenerate_heads():
+    rng = np.random.default_rng(33)
+    q = np.zeros((6, 4, 512), np.uint16)
+    q[0, 1] = 0x8000
+    q[1, 0] = synth.f32_to_bf16_bits(np.full(512, 3.0, np.float32))
+    q[2, 2] = synth.f32_to_bf16_bits(rng.standard_normal(512).astype(np.float32) * 1e15)
+    q[3, 3] = synth.f32_to_bf16_bits(rng.standard_normal(512).astype(np.float32) * 1e-20)
+    q[4] = synth.f32_to_bf16_bits(rng.standard_normal((4, 512)).astype(np.float32))
+    q[5, :, ::5] = 0x3F80
+    w = synth.uniform_bf16((512,), 33, synth.T_W, 0.5, 1.5)
+    pos = np.array([0, 1, 2, 100, 4095, 7], np.int64)
+    qnr_check(q, w, pos, synth.cos_sin_cache(4096), 6, 1e-6, "degenerate")
+
+
+def test_qnr_bad_position_poisons_only_its_token():
+    cfg = dict(synth.QNR_FORWARD, N=6, Hq=3, Hpad=4, seed=34)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    bad = pos.copy()
+    bad[2] = -5
+    got = qnr_gpu(q, w, bad, cache, 4, 1e-6)
+    good = [0, 1, 3, 4, 5]
+    exp = oracle.qnorm_rope(q[good].copy(), w, pos[good].copy(), cache, 4, 1e-6)
+    assert (got[good] == exp).all()
+    assert (got[2, :3] == 0x7FC0).all() and (got[2, 3] == 0).all()
+
+
+# --------------------------------------------------- kv_rope_quant_insert
+
+def kvi_gpu(kv, pos, cache, slots, nb, bs, stride, scale_fmt="fp32", fill=0xAA):
+    k_big = torch.full((nb, stride), fill, dtype=torch.uint8, device=DEV)
+    rq.kv_rope_quant_insert(dev(kv), dev(pos), dev(cache), dev(slots), k_big, bs, scale_fmt)
+    torch.cuda.synchronize()
+    return host(k_big)
+
+
+def kvi_check(kv, pos, cache, slots, nb, bs, stride=None, scale_fmt="fp32", what="",
+              oracle_slots=None):
+    stride = bs * 528 if stride is None else stride
+    print(f"[case] kvi {what} N={kv.shape[0]} blocks={nb}x{bs} stride={stride} "
+          f"fmt={scale_fmt}", flush=True)
+    got = kvi_gpu(kv, pos, cache, slots, nb, bs, stride, scale_fmt)
+    exp = np.full((nb, stride), 0xAA, np.uint8)
+    oracle.kv_rope_quant_insert(kv, pos, cache, slots if oracle_slots is None else oracle_slots,
+                                exp, bs, stride, FMT[scale_fmt])
+    # placement, untouched bytes and scale bytes must be exact; codes to the bar
+    diff = got != exp
+    rec = np.zeros_like(diff)
+    flat_slots = slots if oracle_slots is None else oracle_slots
+    for s in flat_slots[flat_slots >= 0]:
+        off = (s // bs) * stride + (s % bs) * 528
+        rec.reshape(-1)[off:off + 512] = True
+    assert not (diff & ~rec).any(), "bytes outside the code fields differ"
+    assert_codes_match(got[rec], exp[rec], f"kvi {what} codes")
+    return got
+
+
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_kvi_forward_full_size(scale_fmt):
+    cfg = synth.KVI_FORWARD
+    kv, pos, slots, cache = synth.kvi_inputs(cfg)
+    kvi_check(kv, pos, cache, slots, cfg["num_blocks"], cfg["block_size"], None, scale_fmt,
+              "forward 8192 -> 256x64")
+
+
+@pytest.mark.parametrize("threads", [64, 256])
+def test_kvi_holes_gaps_and_out_of_range(threads):
+    rq.set_block_threads(threads)
+    N, nb, bs = 45, 5, 16
+    kv = synth.normal_bf16((N, 512), 35, synth.T_KV)
+    pos = synth.uniform_positions(N, 65536, 35)
+    slots = synth.slot_permutation(N, nb * bs, 35)
+    slots[[3, 10, 44]] = -1
+    slots[[7, 20]] = [nb * bs, 10 ** 12]  # no such slot: skipped by the kernel
+    o_slots = slots.copy()
+    o_slots[[7, 20]] = -1
+    kvi_check(kv, pos, synth.cos_sin_cache(65536), slots, nb, bs, bs * 528 + 64, "fp32",
+              f"holes threads={threads}", oracle_slots=o_slots)
+
+
+def test_kvi_bad_position_poisons_its_record():
+    N, nb, bs = 8, 2, 8
+    kv = synth.normal_bf16((N, 512), 36, synth.T_KV)
+    pos = np.arange(N, dtype=np.int64)
+    slots = synth.slot_permutation(N, nb * bs, 36)
+    cache = synth.cos_sin_cache(64)
+    bad = pos.copy()
+    bad[4] = 64
+    got = kvi_gpu(kv, bad, cache, slots, nb, bs, bs * 528)
+    o_slots = slots.copy()
+    o_slots[4] = -1
+    exp = np.full((nb, bs * 528), 0xAA, np.uint8)
+    oracle.kv_rope_quant_insert(kv, pos, cache, o_slots, exp, bs)
+    s = slots[4]
+    off = (s // bs) * bs * 528 + (s % bs) * 528
+    g = got.reshape(-1)
+    assert (g[off:off + 512] == 0x7F).all()
+    assert np.isnan(g[off + 512:off + 528].view(np.float32)).all()
+    g[off:off + 528] = 0xAA
+    assert (got == exp).all()
