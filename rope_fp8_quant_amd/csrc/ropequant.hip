@@ -111,8 +111,65 @@ __device__ __forceinline__ void unpack_bf16(const uint4 (&w)[4], Vals& v) {
   }
 }
 
-// cos/sin for the lane's rotated pairs (lanes 12..15 only): cs[0] = cos of
-// pairs in chunk k=2, cs[1] = cos for k=3, cs[2], cs[3] = the matching sin.
+// ---- staging: contiguous HBM reads, then the per-lane layout through LDS
+//
+// Each wave owns 4 KiB of LDS: one 1 KiB row per unit.  A wave first reads
+// its 4 units' rows with 16-byte nontemporal loads whose 64 lanes cover one
+// whole 1 KiB row per instruction (full cache lines per instruction, which
+// is what lets the streaming reads run near the HBM peak), writes them to
+// LDS, and each 16-lane row then reads back its unit's 4 chunks per lane.
+// 16-byte slot s of a unit row is stored at LDS slot s ^ (((s >> 4) & 3) << 2):
+// the 16 lanes of a row then read 16 different bank groups for each of
+// their 4 reads, and the writes stay conflict-free too.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t* global_u32x4_ptr;
+
+// 16-byte nontemporal load from global memory (the explicit address space
+// keeps it a global_load rather than a flat one).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((global_u32x4_ptr)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  // LDS operations of one wave complete in issue order; these keep the
+  // compiler from moving the reads above the writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// rows[k] = first element of unit k's 512-dim bf16 row, or nullptr if the
+// wave has no unit k to read (wave-uniform).  issue_rows starts the four 1 KiB
+// reads; transpose_rows parks them in LDS and hands lane L of row q, in w[m],
+// the 8 bf16 of dims lane_dim0(L) + 32m of unit q.
+__device__ __forceinline__ void issue_rows(const uint16_t* const (&rows)[4], int lane,
+                                           uint4 (&raw)[4]) {
+  if (rows[0] && rows[1] && rows[2] && rows[3]) {  // the common, branch-free case
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      raw[k] = rows[k] ? load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+__device__ __forceinline__ void transpose_rows(uint4* lds_wave, const uint4 (&raw)[4], int lane,
+                                               uint4 (&w)[4]) {
+  const int wslot = lane ^ (((lane >> 4) & 3) << 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) lds_wave[64 * k + wslot] = raw[k];
+  wave_lds_sync();
+  const int q = lane >> 4, L = lane & 15, b = L >> 2, r = L & 3;
+  // slot 16b + r + 4m lives at 16b + r + 4(m ^ b)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) w[m] = lds_wave[64 * q + 16 * b + r + 4 * (m ^ b)];
+}
+
+// cos/sin for the lane's rotated pairs (lanes 12..15 only): c[0] = cos of
+// the 4 pairs in chunk k=2, c[1] = cos for k=3; s[] the matching sin.
 struct RopeCS {
   float4 c[2];
   float4 s[2];
@@ -186,7 +243,9 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         q[e] = __builtin_amdgcn_fmed3f(v.x[k][4 * h + e] * mult, -kE4m3Max, kE4m3Max);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      // bytes 2..3 of the first result are overwritten by the second convert,
+      // so any register serves as its "old" operand
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __builtin_bit_cast(int, q[0]), false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
       codes[2 * k + h] = (uint32_t)w;
     }
@@ -202,9 +261,16 @@ __device__ __forceinline__ uint32_t pack_ue8m0(uint32_t ebyte, int q) {
   return w;
 }
 
+// Wave index in the grid, made wave-uniform (so row addresses live in SGPRs).
+// wpb_log2 = log2(waves per workgroup), passed by the host.
+__device__ __forceinline__ uint32_t wave_index(uint32_t wpb_log2) {
+  return __builtin_amdgcn_readfirstlane((xcd_block_id() << wpb_log2) + (threadIdx.x >> 6));
+}
+
 // --------------------------------------------------------------- kernels
 
 struct IrqParams {
+  uint32_t wpb_log2;  // log2(waves per workgroup)
   const uint16_t* o;
   int64_t o_st, o_sh;
   const int64_t* positions;
@@ -220,62 +286,115 @@ struct IrqParams {
   int64_t sc_sg, sc_st, sc_sb;
 };
 
+// Row q of the wave picks its value out of the four wave-uniform ones.
+// (Two levels of selects on the bits of q; the four values are passed
+// separately so they stay in registers.)
+template <typename T>
+__device__ __forceinline__ T pick_row(int q, T v0, T v1, T v2, T v3) {
+  const bool odd = (q & 1) != 0, high = (q & 2) != 0;
+  const T lo = odd ? v1 : v0;
+  const T hi = odd ? v3 : v2;
+  return high ? hi : lo;
+}
+#define PICK_ROW(q, a) pick_row((q), (a)[0], (a)[1], (a)[2], (a)[3])
+
 template <int FMT>
 __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
-  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
-  const uint32_t unit = tid >> 4;
-  const int L = threadIdx.x & 15;
-  if (unit >= p.units) return;  // whole rows only: DPP never reads a retired lane
-  const uint32_t t = magic_div(unit, p.div_heads);
-  const uint32_t h = unit - t * p.n_heads;
-  const uint32_t g = magic_div(h, p.div_hpg);
-  const uint32_t j = h - g * p.hpg;
-  const int d0 = lane_dim0(L);
-
-  const int64_t pos = p.positions[t];
-  const bool bad = pos < 0 || pos >= p.max_pos;
-  const uint4* src = reinterpret_cast<const uint4*>(p.o + (int64_t)t * p.o_st +
-                                                    (int64_t)h * p.o_sh + d0);
-  uint4 w[4];
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, L = lane & 15;
+  const uint32_t unit0 = wave_index(p.wpb_log2) * 4u;
+  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  // The wave's four units, all wave-uniform (scalar registers and loads).
+  // A tail wave repeats its last unit in the missing slots: every read stays
+  // inside the tensors, and slots without a unit store nothing.
+  const uint16_t* rows[4];
+  uint32_t tk[4], hk[4];
+  int64_t posk[4];
+  uint8_t* outk[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
-  RopeCS cs;
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u = min(unit0 + k, p.units - 1u);
+    tk[k] = magic_div(u, p.div_heads);
+    hk[k] = u - tk[k] * p.n_heads;
+    rows[k] = p.o + (int64_t)tk[k] * p.o_st + (int64_t)hk[k] * p.o_sh;
+    posk[k] = p.positions[tk[k]];
+    const uint32_t g = magic_div(hk[k], p.div_hpg);
+    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)tk[k] * p.out_st +
+              (int64_t)(hk[k] - g * p.hpg) * kHeadDim;
+  }
+  uint4 raw[4], w[4];
+  issue_rows(rows, lane, raw);
+
+  const bool valid = unit0 + q < p.units;
+  const uint32_t t = PICK_ROW(q, tk), h = PICK_ROW(q, hk);
+  const int64_t pos = PICK_ROW(q, posk);
+  const bool bad = pos < 0 || pos >= p.max_pos;
   const bool rope = L >= 12;
-  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  // every lane reads its unit's cos/sin (cached; only lanes 12..15 use it):
+  // unconditional loads keep the memory counters' order fixed
+  RopeCS cs;
+  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  transpose_rows(lds_wave, raw, lane, w);
 
   Vals v;
   unpack_bf16(w, v);
   if (rope) rope_lane<true>(v, cs);
-
   float scale;
   uint32_t ebyte, codes[8];
   quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
-  const int q = L >> 2;
+  const int blk = L >> 2, r = L & 3;
   uint32_t word = 0;
-  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, q);
-  if (bad) {
+  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
+  if (bad) {  // position outside the table: the unit is written as NaN
 #pragma unroll
     for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
     scale = __builtin_nanf("");
     word = 0xFFFFFFFFu;
   }
 
-  uint8_t* dst = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim + d0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<uint2*>(dst + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
-  if (FMT == RQ_SCALE_UE8M0) {
-    if (L == 0)
-      static_cast<uint32_t*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                                       (int64_t)j * p.sc_sb] = word;
-  } else {
-    if ((L & 3) == 0)
+  // scales: one 4-byte store per block (any layout the strides describe)
+  if (valid) {
+    const uint32_t g = magic_div(h, p.div_hpg);
+    const uint32_t j = h - g * p.hpg;
+    if (FMT == RQ_SCALE_UE8M0) {
+      if (L == 0)
+        static_cast<uint32_t*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                                         (int64_t)j * p.sc_sb] = word;
+    } else if (r == 0) {
       static_cast<float*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                                    (int64_t)(j * 4 + q) * p.sc_sb] = scale;
+                                    (int64_t)(j * 4 + blk) * p.sc_sb] = scale;
+    }
   }
+
+  // codes: through LDS so that each store writes a unit's 512 contiguous
+  // bytes.  8-byte granule G of unit q sits at G ^ ((((G >> 4) & 3) ^ (q & 1)) << 2),
+  // which keeps both the per-lane writes and the row reads free of bank
+  // conflicts.
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+  uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int G = 16 * blk + r + 4 * m;
+    lds8[64 * q + (G ^ (((blk ^ (q & 1)) & 3) << 2))] = make_uint2(codes[2 * m], codes[2 * m + 1]);
+  }
+  wave_lds_sync();
+  const int half = lane >> 5, j16 = lane & 31;
+  // lanes 0..31 store unit 2i, lanes 32..63 unit 2i+1 (constant indices
+  // throughout, so the base pointers stay in registers)
+  uint8_t* const base01 = half ? outk[1] : outk[0];
+  uint8_t* const base23 = half ? outk[3] : outk[2];
+  const int G0 = 2 * j16;
+  const int sw = (G0 >> 4) & 3;
+  const uint4 c01 = *reinterpret_cast<const uint4*>(lds8 + 64 * half + (G0 ^ ((sw ^ half) << 2)));
+  const uint4 c23 =
+      *reinterpret_cast<const uint4*>(lds8 + 64 * (2 + half) + (G0 ^ ((sw ^ half) << 2)));
+  if (unit0 + half < p.units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
+  if (unit0 + 2 + half < p.units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
 }
 
 struct QnrParams {
+  uint32_t wpb_log2;  // log2(waves per workgroup)
   const uint16_t* q;
   int64_t q_st, q_sh;
   const uint16_t* weight;
@@ -291,93 +410,123 @@ struct QnrParams {
 
 template <bool HAS_WEIGHT>
 __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
-  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
-  const uint32_t unit = tid >> 4;
-  const int L = threadIdx.x & 15;
-  if (unit >= p.units) return;
-  const uint32_t t = magic_div(unit, p.div_hpad);
-  const uint32_t h = unit - t * p.hpad;
-  const int d0 = lane_dim0(L);
-  uint4* dst = reinterpret_cast<uint4*>(p.q_out + (int64_t)unit * kHeadDim + d0);
-
-  if (h >= p.hq) {  // pad head: exact +0 ([P1] section 1)
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, L = lane & 15;
+  const uint32_t unit0 = wave_index(p.wpb_log2) * 4u;
+  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint16_t* rows[4];
+  uint32_t livek[4];
+  int64_t posk[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dst[4 * k] = make_uint4(0u, 0u, 0u, 0u);
-    return;
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u = min(unit0 + k, p.units - 1u);
+    const uint32_t t = magic_div(u, p.div_hpad);
+    const uint32_t h = u - t * p.hpad;
+    livek[k] = (unit0 + k < p.units && h < p.hq) ? 1u : 0u;
+    rows[k] = livek[k] ? p.q + (int64_t)t * p.q_st + (int64_t)h * p.q_sh : nullptr;
+    posk[k] = p.positions[t];
   }
+  uint4 raw[4], w[4];
+  issue_rows(rows, lane, raw);
 
-  const int64_t pos = p.positions[t];
+  const bool live = PICK_ROW(q, livek) != 0;
+  const int64_t pos = PICK_ROW(q, posk);
   const bool bad = pos < 0 || pos >= p.max_pos;
-  const uint4* src = reinterpret_cast<const uint4*>(p.q + (int64_t)t * p.q_st +
-                                                    (int64_t)h * p.q_sh + d0);
-  uint4 w[4], wt[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
+  const bool rope = L >= 12;
+  const int d0 = lane_dim0(L);
+  // weight and cos/sin are read by every lane (cached): unconditional loads
+  // keep the memory counters' order fixed
+  uint4 wt[4];
   if (HAS_WEIGHT) {
     const uint4* wp = reinterpret_cast<const uint4*>(p.weight + d0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) wt[k] = wp[4 * k];
   }
   RopeCS cs;
-  const bool rope = L >= 12;
-  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  transpose_rows(lds_wave, raw, lane, w);
 
-  Vals v;
-  unpack_bf16(w, v);
+  uint4 outv[4];
+  if (live) {
+    Vals v;
+    unpack_bf16(w, v);
 
-  // Sum of squares in the fixed tree: chunk sums left to right, then
-  // butterflies over the chunk index c = 16q + 4k + r for bit 0, 1 (lanes
-  // r^1, r^2), bit 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads q^1, q^2).
-  float ps[4];
+    // Sum of squares in the fixed tree: chunk sums left to right, then
+    // butterflies over the chunk index c = 16q + 4k + r for bit 0, 1 (lanes
+    // r^1, r^2), bit 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads q^1, q^2).
+    float ps[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float acc = v.x[k][0] * v.x[k][0];
+    for (int k = 0; k < 4; ++k) {
+      float acc = v.x[k][0] * v.x[k][0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
-    ps[k] = acc;
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap2>(ps[k]);
-  float ss = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  ss = ss + dpp_f32<kRowHalfMirror>(ss);
-  ss = ss + dpp_f32<kRowMirror>(ss);
-  const float mean = ss * (1.0f / 512.0f);
-  const float r = 1.0f / sqrtf(mean + p.eps);
-
-  if (HAS_WEIGHT) {
-    Vals wv;
-    unpack_bf16(wt, wv);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * r) * wv.x[k][e];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * r;
-  }
-  if (rope) rope_lane<false>(v, cs);
-
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t o4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x2 f = {v.x[k][2 * i], v.x[k][2 * i + 1]};
-      o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+      for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
+      ps[k] = acc;
     }
-    uint4 outv = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-    if (bad) outv = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    dst[4 * k] = outv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap2>(ps[k]);
+    float ss = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    ss = ss + dpp_f32<kRowHalfMirror>(ss);
+    ss = ss + dpp_f32<kRowMirror>(ss);
+    const float mean = ss * (1.0f / 512.0f);
+    const float rs = 1.0f / sqrtf(mean + p.eps);
+
+    if (HAS_WEIGHT) {
+      Vals wv;
+      unpack_bf16(wt, wv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * rs) * wv.x[k][e];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * rs;
+    }
+    if (rope) rope_lane<false>(v, cs);
+
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t o4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 f = {v.x[k][2 * i], v.x[k][2 * i + 1]};
+        o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+      }
+      outv[k] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+    if (bad) {  // position outside the table: the head is written as NaN
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    }
+  } else {  // pad head (or no unit): exact +0 ([P1] section 1)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) outv[k] = make_uint4(0u, 0u, 0u, 0u);
   }
+
+  // Back through LDS (same slot swizzle as the input side) so that each store
+  // writes one unit's 1 KiB; the wave's 4 units are 4 KiB of contiguous q_out.
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+  const int b = L >> 2, r = L & 3;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) lds_wave[64 * q + 16 * b + r + 4 * (m ^ b)] = outv[m];
+  wave_lds_sync();
+  const int rslot = lane ^ (((lane >> 4) & 3) << 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (unit0 + k < p.units)
+      reinterpret_cast<uint4*>(p.q_out + (int64_t)(unit0 + k) * kHeadDim)[lane] =
+          lds_wave[64 * k + rslot];
 }
 
 struct KviParams {
+  uint32_t wpb_log2;  // log2(waves per workgroup)
   const uint16_t* kv;
   int64_t kv_st;
   const int64_t* positions;
@@ -395,23 +544,33 @@ struct KviParams {
 
 template <int FMT>
 __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
-  const uint32_t tid = xcd_block_id() * blockDim.x + threadIdx.x;
-  const uint32_t t = tid >> 4;
-  const int L = threadIdx.x & 15;
-  if (t >= p.n_tokens) return;
-  const int64_t slot = p.slots[t];
-  if (slot < 0 || slot >= p.num_slots) return;  // padding token, or no such slot
-  const int d0 = lane_dim0(L);
-
-  const int64_t pos = p.positions[t];
-  const bool bad = pos < 0 || pos >= p.max_pos;
-  const uint4* src = reinterpret_cast<const uint4*>(p.kv + (int64_t)t * p.kv_st + d0);
-  uint4 w[4];
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int qr = lane >> 4, L = lane & 15;
+  const uint32_t t0 = wave_index(p.wpb_log2) * 4u;
+  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint16_t* rows[4];
+  int64_t slotk[4], posk[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = src[4 * k];
-  RopeCS cs;
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t t = min(t0 + k, p.n_tokens - 1u);
+    slotk[k] = (t0 + k < p.n_tokens) ? p.slots[t] : -1;
+    posk[k] = p.positions[t];
+    rows[k] = (slotk[k] >= 0 && slotk[k] < p.num_slots) ? p.kv + (int64_t)t * p.kv_st : nullptr;
+  }
+  uint4 raw[4], w[4];
+  issue_rows(rows, lane, raw);
+
+  const int64_t slot = PICK_ROW(qr, slotk);
+  const int64_t pos = PICK_ROW(qr, posk);
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  const bool use = slot >= 0 && slot < p.num_slots;  // else: padding token, or no such slot
   const bool rope = L >= 12;
-  if (rope) load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  RopeCS cs;
+  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);  // unconditional, as above
+  transpose_rows(lds_wave, raw, lane, w);
+  if (!use) return;
+  const int d0 = lane_dim0(L);
 
   Vals v;
   unpack_bf16(w, v);
@@ -423,7 +582,7 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   const int q = L >> 2;
   uint32_t word = 0;
   if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, q);
-  if (bad) {
+  if (bad) {  // position outside the table: the record is written as NaN
 #pragma unroll
     for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
     scale = __builtin_nanf("");
@@ -496,13 +655,16 @@ bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
   return true;
 }
 
+// Every params struct starts with wpb_log2, filled in here.
 int launch(const void* fn, uint32_t units, void* params, hipStream_t stream) {
   const int threads = pick_block_threads(units);
+  *static_cast<uint32_t*>(params) = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
   const uint32_t per_block = (uint32_t)threads / 16u;
   const uint32_t blocks = (units + per_block - 1) / per_block;
   void* args[] = {params};
+  const size_t lds_bytes = (size_t)(threads / 64) * 4096;  // 4 KiB staging per wave
   const hipError_t e =
-      hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, 0, stream);
+      hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, lds_bytes, stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
