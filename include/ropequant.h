@@ -38,9 +38,11 @@
  *     [0, max_pos); slots unique and below num_blocks * cache_block_size;
  *     input values finite (and |q| < 2^59 for qnorm_rope).  The kernels never
  *     access memory outside the described tensors even when the contract is
- *     broken: a unit whose position is out of range is written as NaN (e4m3
- *     0x7F codes with NaN scales, or bf16 0x7FC0), and a slot outside
- *     [0, num_blocks * cache_block_size) is skipped.
+ *     broken: a unit whose position is out of range gets NaN scales (fp32
+ *     NaN, or UE8M0 exponent bytes 0xFF), so every value it dequantizes to is
+ *     NaN, its codes being unspecified; qnorm_rope writes such a head as bf16
+ *     NaN (0x7FC0); and a slot outside [0, num_blocks * cache_block_size) is
+ *     skipped.
  *   - Strides are in elements of the tensor's own type unless "bytes" is said.
  *   - Arithmetic: every fp32 step is an IEEE-754 basic operation rounded to
  *     nearest even, with no fused multiply-add; division and square root are

@@ -139,21 +139,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// rows[k] = first element of unit k's 512-dim bf16 row, or nullptr if the
-// wave has no unit k to read (wave-uniform).  issue_rows starts the four 1 KiB
-// reads; transpose_rows parks them in LDS and hands lane L of row q, in w[m],
-// the 8 bf16 of dims lane_dim0(L) + 32m of unit q.
+// rows[k] = first element of unit k's 512-dim bf16 row (wave-uniform; the
+// kernels substitute a row they do read for any slot without a unit, so the
+// four loads are unconditional).  issue_rows starts the four 1 KiB reads;
+// transpose_rows parks them in LDS and hands lane L of row q, in w[m], the
+// 8 bf16 of dims lane_dim0(L) + 32m of unit q.
 __device__ __forceinline__ void issue_rows(const uint16_t* const (&rows)[4], int lane,
                                            uint4 (&raw)[4]) {
-  if (rows[0] && rows[1] && rows[2] && rows[3]) {  // the common, branch-free case
 #pragma unroll
-    for (int k = 0; k < 4; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      raw[k] = rows[k] ? load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane)
-                       : make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int k = 0; k < 4; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
 }
 
 __device__ __forceinline__ void transpose_rows(uint4* lds_wave, const uint4 (&raw)[4], int lane,
@@ -239,10 +233,12 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
   for (int k = 0; k < 4; ++k) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      // No clamp is needed before the convert: |x * mult| <= 448 * (1 + 2^-24)^3
+      // < 448.0001 (two roundings of the scale, one of the product), and the
+      // convert rounds to nearest even, giving 448 for every value up to 464.
       float q[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        q[e] = __builtin_amdgcn_fmed3f(v.x[k][4 * h + e] * mult, -kE4m3Max, kE4m3Max);
+      for (int e = 0; e < 4; ++e) q[e] = v.x[k][4 * h + e] * mult;
       // bytes 2..3 of the first result are overwritten by the second convert,
       // so any register serves as its "old" operand
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __builtin_bit_cast(int, q[0]), false);
@@ -302,68 +298,66 @@ template <int FMT>
 __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, L = lane & 15;
+  const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
   const uint32_t unit0 = wave_index(p.wpb_log2) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   // The wave's four units, all wave-uniform (scalar registers and loads).
   // A tail wave repeats its last unit in the missing slots: every read stays
   // inside the tensors, and slots without a unit store nothing.
   const uint16_t* rows[4];
-  uint32_t tk[4], hk[4];
+  const float* csk[4];
   int64_t posk[4];
+  uint32_t badk[4];
   uint8_t* outk[4];
+  uint8_t* sck[4];  // the unit's first scale
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t u = min(unit0 + k, p.units - 1u);
-    tk[k] = magic_div(u, p.div_heads);
-    hk[k] = u - tk[k] * p.n_heads;
-    rows[k] = p.o + (int64_t)tk[k] * p.o_st + (int64_t)hk[k] * p.o_sh;
-    posk[k] = p.positions[tk[k]];
-    const uint32_t g = magic_div(hk[k], p.div_hpg);
-    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)tk[k] * p.out_st +
-              (int64_t)(hk[k] - g * p.hpg) * kHeadDim;
+    const uint32_t t = magic_div(u, p.div_heads);
+    const uint32_t h = u - t * p.n_heads;
+    const uint32_t g = magic_div(h, p.div_hpg);
+    const uint32_t j = h - g * p.hpg;
+    rows[k] = p.o + (int64_t)t * p.o_st + (int64_t)h * p.o_sh;
+    posk[k] = p.positions[t];
+    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim;
+    const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                          (int64_t)(FMT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
+    sck[k] = static_cast<uint8_t*>(p.scales) + 4 * first;
   }
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
-
-  const bool valid = unit0 + q < p.units;
-  const uint32_t t = PICK_ROW(q, tk), h = PICK_ROW(q, hk);
-  const int64_t pos = PICK_ROW(q, posk);
-  const bool bad = pos < 0 || pos >= p.max_pos;
-  const bool rope = L >= 12;
+  // (positions are used only after the row reads are on their way, so the
+  // four scalar loads overlap them instead of running one after another)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
+    badk[k] = bad;
+    csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+  }
   // every lane reads its unit's cos/sin (cached; only lanes 12..15 use it):
   // unconditional loads keep the memory counters' order fixed
   RopeCS cs;
-  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  load_cs(PICK_ROW(q, csk), r, cs);
   transpose_rows(lds_wave, raw, lane, w);
 
   Vals v;
   unpack_bf16(w, v);
-  if (rope) rope_lane<true>(v, cs);
+  if (L >= 12) rope_lane<true>(v, cs);
   float scale;
   uint32_t ebyte, codes[8];
   quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
-  const int blk = L >> 2, r = L & 3;
-  uint32_t word = 0;
-  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
-  if (bad) {  // position outside the table: the unit is written as NaN
-#pragma unroll
-    for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
-    scale = __builtin_nanf("");
-    word = 0xFFFFFFFFu;
-  }
 
-  // scales: one 4-byte store per block (any layout the strides describe)
-  if (valid) {
-    const uint32_t g = magic_div(h, p.div_hpg);
-    const uint32_t j = h - g * p.hpg;
+  // scales: one 4-byte store per block (any layout the strides describe).  A
+  // unit whose position is outside the table gets NaN scales, which turns all
+  // of its dequantized values into NaN.
+  if (unit0 + q < p.units) {
+    const bool bad = PICK_ROW(q, badk) != 0;
+    uint8_t* sc = PICK_ROW(q, sck);
     if (FMT == RQ_SCALE_UE8M0) {
-      if (L == 0)
-        static_cast<uint32_t*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                                         (int64_t)j * p.sc_sb] = word;
+      const uint32_t word = pack_ue8m0(ebyte, blk);
+      if (L == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
     } else if (r == 0) {
-      static_cast<float*>(p.scales)[(int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                                    (int64_t)(j * 4 + blk) * p.sc_sb] = scale;
+      reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = bad ? __builtin_nanf("") : scale;
     }
   }
 
@@ -379,9 +373,9 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     lds8[64 * q + (G ^ (((blk ^ (q & 1)) & 3) << 2))] = make_uint2(codes[2 * m], codes[2 * m + 1]);
   }
   wave_lds_sync();
-  const int half = lane >> 5, j16 = lane & 31;
   // lanes 0..31 store unit 2i, lanes 32..63 unit 2i+1 (constant indices
   // throughout, so the base pointers stay in registers)
+  const int half = lane >> 5, j16 = lane & 31;
   uint8_t* const base01 = half ? outk[1] : outk[0];
   uint8_t* const base23 = half ? outk[3] : outk[2];
   const int G0 = 2 * j16;
@@ -424,11 +418,12 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
     const uint32_t t = magic_div(u, p.div_hpad);
     const uint32_t h = u - t * p.hpad;
     livek[k] = (unit0 + k < p.units && h < p.hq) ? 1u : 0u;
-    rows[k] = livek[k] ? p.q + (int64_t)t * p.q_st + (int64_t)h * p.q_sh : nullptr;
+    rows[k] = p.q + (int64_t)t * p.q_st + (int64_t)min(h, p.hq - 1u) * p.q_sh;
     posk[k] = p.positions[t];
   }
-  uint4 raw[4], w[4];
-  issue_rows(rows, lane, raw);
+  // A wave of pad heads only reads nothing (its rows in LDS are never used).
+  uint4 raw[4] = {}, w[4];
+  if (livek[0] | livek[1] | livek[2] | livek[3]) issue_rows(rows, lane, raw);
 
   const bool live = PICK_ROW(q, livek) != 0;
   const int64_t pos = PICK_ROW(q, posk);
@@ -546,61 +541,62 @@ template <int FMT>
 __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
-  const int qr = lane >> 4, L = lane & 15;
+  const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
   const uint32_t t0 = wave_index(p.wpb_log2) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   const uint16_t* rows[4];
-  int64_t slotk[4], posk[4];
+  const float* csk[4];
+  int64_t posk[4];
+  uint32_t badk[4];
+  uint8_t* reck[4];  // the token's 528-byte record, or nullptr: nothing to write
+  int64_t slotk[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t t = min(t0 + k, p.n_tokens - 1u);
-    slotk[k] = (t0 + k < p.n_tokens) ? p.slots[t] : -1;
+    slotk[k] = p.slots[t];
+    if (t0 + k >= p.n_tokens) slotk[k] = -1;
+    rows[k] = p.kv + (int64_t)t * p.kv_st;
     posk[k] = p.positions[t];
-    rows[k] = (slotk[k] >= 0 && slotk[k] < p.num_slots) ? p.kv + (int64_t)t * p.kv_st : nullptr;
   }
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
-
-  const int64_t slot = PICK_ROW(qr, slotk);
-  const int64_t pos = PICK_ROW(qr, posk);
-  const bool bad = pos < 0 || pos >= p.max_pos;
-  const bool use = slot >= 0 && slot < p.num_slots;  // else: padding token, or no such slot
-  const bool rope = L >= 12;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // slots and positions used only now (see irq_kernel)
+    const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
+    badk[k] = bad;
+    csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+    reck[k] = nullptr;
+    if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
+      const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
+      const uint32_t idx = (uint32_t)slotk[k] - blk_i * p.bs;
+      reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
+    }
+  }
   RopeCS cs;
-  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);  // unconditional, as above
+  load_cs(PICK_ROW(q, csk), r, cs);  // unconditional, as above
   transpose_rows(lds_wave, raw, lane, w);
-  if (!use) return;
+  uint8_t* const rec = PICK_ROW(q, reck);
+  if (!rec) return;  // whole rows only
   const int d0 = lane_dim0(L);
 
   Vals v;
   unpack_bf16(w, v);
-  if (rope) rope_lane<false>(v, cs);
-
+  if (L >= 12) rope_lane<false>(v, cs);
   float scale;
   uint32_t ebyte, codes[8];
   quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
-  const int q = L >> 2;
   uint32_t word = 0;
-  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, q);
-  if (bad) {  // position outside the table: the record is written as NaN
-#pragma unroll
-    for (int i = 0; i < 8; ++i) codes[i] = 0x7F7F7F7Fu;
-    scale = __builtin_nanf("");
-    word = 0xFFFFFFFFu;
-  }
-
-  const uint32_t s32 = (uint32_t)slot;
-  const uint32_t blk = magic_div(s32, p.div_bs);
-  const uint32_t idx = s32 - blk * p.bs;
-  uint8_t* rec = p.cache + (int64_t)blk * p.block_stride + (int64_t)idx * kRecordBytes;
+  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
-  if ((L & 3) == 0) {
+  if (r == 0) {
+    // a token whose position is outside the table gets NaN scales
+    const bool bad = PICK_ROW(q, badk) != 0;
     uint32_t tail;
-    if (FMT == RQ_SCALE_UE8M0) tail = (q == 0) ? word : 0u;
-    else tail = __builtin_bit_cast(uint32_t, scale);
-    *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * q) = tail;
+    if (FMT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
+    else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
+    *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * blk) = tail;
   }
 }
 

@@ -183,20 +183,25 @@ def test_irq_degenerate_values(scale_fmt):
     check(o, pos, cache, 4, scale_fmt, what="degenerate")
 
 
-def test_irq_bad_position_poisons_only_its_token():
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_irq_bad_position_poisons_only_its_token(scale_fmt):
     cfg = dict(synth.IRQ_TINY, N=12, H=8, hpg=4, seed=82)
     o, pos, cache = synth.irq_inputs(cfg)
     bad = pos.copy()
     bad[5] = cache.shape[0]
     bad[9] = -1
-    print("[case] irq bad positions", flush=True)
-    out, sc = run_gpu(o, bad, cache, 4)
+    print(f"[case] irq bad positions fmt={scale_fmt}", flush=True)
+    out, sc = run_gpu(o, bad, cache, 4, scale_fmt)
     good = [t for t in range(12) if t not in (5, 9)]
-    eo, es = oracle.inv_rope_fp8_quant(o[good].copy(), pos[good].copy(), cache, 4)
+    eo, es = oracle.inv_rope_fp8_quant(o[good].copy(), pos[good].copy(), cache, 4,
+                                       FMT[scale_fmt])
     assert (out[:, good] == eo).all()
     assert_bits_equal(sc[:, good], es, "good tokens")
-    for t in (5, 9):
-        assert (out[:, t] == 0x7F).all() and np.isnan(sc[:, t]).all()
+    for t in (5, 9):  # NaN scales make every dequantized value NaN
+        if scale_fmt == "fp32":
+            assert np.isnan(sc[:, t]).all()
+        else:
+            assert (sc[:, t] == 0xFFFFFFFF).all()
 
 
 def test_irq_zero_tokens_is_a_no_op():
