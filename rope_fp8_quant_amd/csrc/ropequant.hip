@@ -59,14 +59,21 @@ __device__ __forceinline__ uint32_t magic_div(uint32_t n, Magic m) {
   return (uint32_t)(((uint64_t)n * m.mul) >> m.shift);
 }
 
-// Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so each XCD
-// sees one contiguous range of units: a token's heads (and its cos/sin row)
-// then stay in one XCD's L2.  A bijection on [0, gridDim.x).
-__device__ __forceinline__ uint32_t xcd_block_id() {
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+// Renumber them so each XCD takes chunks of 2^chunk_log2 consecutive
+// workgroups (chunk i of the grid goes to XCD i mod 8): neighbouring units
+// share an XCD (and so their cos/sin rows share its L2) while all XCDs still
+// sweep the tensors together.  The chunk size is a launch-table entry,
+// measured per kernel (whole-range chunks, plain round-robin and sizes in
+// between were timed).  A bijection on [0, gridDim.x): a tail shorter than
+// 8 chunks keeps the plain order.
+__device__ __forceinline__ uint32_t xcd_block_id(uint32_t chunk_log2) {
   const uint32_t nb = gridDim.x, b = blockIdx.x;
+  const uint32_t full = (nb >> (chunk_log2 + 3)) << (chunk_log2 + 3);
+  if (b >= full) return b;
   const uint32_t xcd = b & 7u, local = b >> 3;
-  const uint32_t q = nb >> 3, r = nb & 7u;
-  return (xcd < r) ? xcd * (q + 1u) + local : r * (q + 1u) + (xcd - r) * q + local;
+  const uint32_t chunk = local >> chunk_log2, within = local & ((1u << chunk_log2) - 1u);
+  return (((chunk << 3) + xcd) << chunk_log2) + within;
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) {
@@ -257,16 +264,22 @@ __device__ __forceinline__ uint32_t pack_ue8m0(uint32_t ebyte, int q) {
   return w;
 }
 
+// Launch shape, filled in by the host: every params struct starts with it.
+struct LaunchHdr {
+  uint32_t wpb_log2;    // log2(waves per workgroup)
+  uint32_t chunk_log2;  // log2(workgroups per XCD chunk)
+};
+
 // Wave index in the grid, made wave-uniform (so row addresses live in SGPRs).
-// wpb_log2 = log2(waves per workgroup), passed by the host.
-__device__ __forceinline__ uint32_t wave_index(uint32_t wpb_log2) {
-  return __builtin_amdgcn_readfirstlane((xcd_block_id() << wpb_log2) + (threadIdx.x >> 6));
+__device__ __forceinline__ uint32_t wave_index(const LaunchHdr& h) {
+  return __builtin_amdgcn_readfirstlane((xcd_block_id(h.chunk_log2) << h.wpb_log2) +
+                                        (threadIdx.x >> 6));
 }
 
 // --------------------------------------------------------------- kernels
 
 struct IrqParams {
-  uint32_t wpb_log2;  // log2(waves per workgroup)
+  LaunchHdr hdr;
   const uint16_t* o;
   int64_t o_st, o_sh;
   const int64_t* positions;
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
-  const uint32_t unit0 = wave_index(p.wpb_log2) * 4u;
+  const uint32_t unit0 = wave_index(p.hdr) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   // The wave's four units, all wave-uniform (scalar registers and loads).
   // A tail wave repeats its last unit in the missing slots: every read stays
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
 }
 
 struct QnrParams {
-  uint32_t wpb_log2;  // log2(waves per workgroup)
+  LaunchHdr hdr;
   const uint16_t* q;
   int64_t q_st, q_sh;
   const uint16_t* weight;
@@ -407,7 +420,7 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15;
-  const uint32_t unit0 = wave_index(p.wpb_log2) * 4u;
+  const uint32_t unit0 = wave_index(p.hdr) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   const uint16_t* rows[4];
   uint32_t livek[4];
@@ -521,7 +534,7 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
 }
 
 struct KviParams {
-  uint32_t wpb_log2;  // log2(waves per workgroup)
+  LaunchHdr hdr;
   const uint16_t* kv;
   int64_t kv_st;
   const int64_t* positions;
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
-  const uint32_t t0 = wave_index(p.wpb_log2) * 4u;
+  const uint32_t t0 = wave_index(p.hdr) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   const uint16_t* rows[4];
   const float* csk[4];
@@ -651,10 +664,13 @@ bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
   return true;
 }
 
-// Every params struct starts with wpb_log2, filled in here.
-int launch(const void* fn, uint32_t units, void* params, hipStream_t stream) {
+// Every params struct starts with a LaunchHdr, filled in here.
+int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
+           hipStream_t stream) {
   const int threads = pick_block_threads(units);
-  *static_cast<uint32_t*>(params) = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
+  LaunchHdr* hdr = static_cast<LaunchHdr*>(params);
+  hdr->wpb_log2 = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
+  hdr->chunk_log2 = chunk_log2;
   const uint32_t per_block = (uint32_t)threads / 16u;
   const uint32_t blocks = (units + per_block - 1) / per_block;
   void* args[] = {params};
@@ -663,6 +679,11 @@ int launch(const void* fn, uint32_t units, void* params, hipStream_t stream) {
       hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, lds_bytes, stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
+
+// XCD chunk sizes (log2 workgroups), timed on MI355X per kernel.
+constexpr uint32_t kIrqChunkLog2 = 6;
+constexpr uint32_t kQnrChunkLog2 = 4;
+constexpr uint32_t kKviChunkLog2 = 4;
 
 }  // namespace
 
@@ -731,7 +752,7 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
   p.scales = scales; p.sc_sg = sc_stride_group; p.sc_st = sc_stride_token; p.sc_sb = sc_stride_block;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)irq_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.units, &p, (hipStream_t)stream);
+  return launch(fn, p.units, kIrqChunkLog2, &p, (hipStream_t)stream);
 }
 
 int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
@@ -758,7 +779,7 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
   p.hq = (uint32_t)n_heads_q; p.hpad = (uint32_t)q_head_padded;
   p.eps = (float)eps; p.q_out = q_out;
   const void* fn = norm_weight ? (const void*)qnr_kernel<true> : (const void*)qnr_kernel<false>;
-  return launch(fn, p.units, &p, (hipStream_t)stream);
+  return launch(fn, p.units, kQnrChunkLog2, &p, (hipStream_t)stream);
 }
 
 int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
@@ -788,7 +809,7 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
   p.cache = k_cache; p.block_stride = block_stride_bytes; p.eps = (float)eps;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)kvi_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.n_tokens, &p, (hipStream_t)stream);
+  return launch(fn, p.n_tokens, kKviChunkLog2, &p, (hipStream_t)stream);
 }
 
 }  // extern "C"
