@@ -129,7 +129,35 @@ def bench_qnr_kvi(args, device, stream):
     return res
 
 
+def graph_per_call_us(fn, calls=100, replays=5):
+    """Per-call time of `calls` launches captured in one HIP graph (median of
+    `replays` replays): the GPU-side cost without Python dispatch."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays + 1):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / calls)
+    times = sorted(times[1:])
+    return times[len(times) // 2]
+
+
 def bench_decode(args, device, stream):
+    """Decode sizes: per call through Python (host-bound) and in a HIP graph."""
     import torch
 
     import rope_fp8_quant_amd as rq
@@ -141,14 +169,22 @@ def bench_decode(args, device, stream):
         o, pos, _ = synth.irq_inputs(cfg)
         od, pd = to_dev(o, device), to_dev(pos, device)
         out, sc = rq.empty_inv_rope_fp8_quant_outputs(N, 32, 8, device)
-        ms = time_launches(lambda: rq.inv_rope_fp8_quant(od, pd, cache, 8, out, sc),
-                           args.steps, args.warmup, stream)
         q = to_dev(synth.normal_bf16((N, 32, 512), 50 + N, synth.T_Q), device)
         q_out = torch.empty((N, 128, 512), dtype=torch.bfloat16, device=device)
-        msq = time_launches(lambda: rq.qnorm_rope(q, None, pd, cache, q_out, 1e-6),
-                            args.steps, args.warmup, stream)
-        res[f"N{N}"] = dict(irq_us=ms * 1e3, irq_gbs=irq_bytes(N, 32) / ms / 1e6,
-                            qnr_us=msq * 1e3, qnr_gbs=qnr_bytes(N, 32, 128) / msq / 1e6)
+
+        def irq():
+            rq.inv_rope_fp8_quant(od, pd, cache, 8, out, sc)
+
+        def qnr():
+            rq.qnorm_rope(q, None, pd, cache, q_out, 1e-6)
+
+        ms = time_launches(irq, 200, 20, stream)
+        msq = time_launches(qnr, 200, 20, stream)
+        gi, gq = graph_per_call_us(irq), graph_per_call_us(qnr)
+        res[f"N{N}"] = dict(irq_us_python=round(ms * 1e3, 2), irq_us_graph=round(gi, 2),
+                            irq_gbs_graph=round(irq_bytes(N, 32) / gi / 1e3, 1),
+                            qnr_us_python=round(msq * 1e3, 2), qnr_us_graph=round(gq, 2),
+                            qnr_gbs_graph=round(qnr_bytes(N, 32, 128) / gq / 1e3, 1))
     return res
 
 
@@ -197,8 +233,10 @@ def traffic_from_profile():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # defaults: the GPU's clocks need ~100 launches (~12 ms) to ramp up
+    # from idle, so the timed region starts after 100 untimed launches
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", choices=["irq", "qnr", "kvi", "decode", "copy"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -56,6 +56,14 @@ def lib():
         L.orc_kv_rope_quant_insert.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, I32,
                                                I32, D]
         L.orc_kv_rope_quant_insert.restype = ctypes.c_int
+        F = ctypes.c_float
+        L.orc_indexer_rope.argtypes = [P, P, P]
+        L.orc_indexer_rope.restype = None
+        L.orc_indexer_head.argtypes = [P, P, F, F, F, F, P, P, P]
+        L.orc_indexer_head.restype = None
+        L.orc_indexer_q_rope_quant.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, I32, D, D,
+                                               D, P, I64, I64, P, I64]
+        L.orc_indexer_q_rope_quant.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -237,3 +245,49 @@ def kv_rope_quant_insert(kv_bits, positions, cos_sin_cache, slot_mapping, k_cach
                                         cache_block_size, scale_fmt, eps)
     _check(rc, "kv_rope_quant_insert")
     return k_cache
+
+
+# ------------------------------------------------------------- indexer
+
+def indexer_rope(x, cs_row):
+    """Rotate-half RoPE (with the bf16 round trip) of one 128-dim fp32 head."""
+    x = _need(np.ascontiguousarray(x, dtype=np.float32), np.float32, "x")
+    cs_row = _need(np.ascontiguousarray(cs_row, dtype=np.float32), np.float32, "cs_row")
+    assert x.shape == (128,) and cs_row.shape == (64,)
+    y = np.empty(128, dtype=np.float32)
+    lib().orc_indexer_rope(_ptr(x), _ptr(cs_row), _ptr(y))
+    return y
+
+
+def indexer_head(x, cs_row, w, softmax_scale, head_scale=1.0, eps=1e-10):
+    """One 128-dim fp32 head -> (codes[128] uint8, w_out f32, q_scale f32)."""
+    x = _need(np.ascontiguousarray(x, dtype=np.float32), np.float32, "x")
+    cs_row = _need(np.ascontiguousarray(cs_row, dtype=np.float32), np.float32, "cs_row")
+    assert x.shape == (128,) and cs_row.shape == (64,)
+    codes = np.empty(128, dtype=np.uint8)
+    wo = np.zeros(1, dtype=np.float32)
+    qs = np.zeros(1, dtype=np.float32)
+    lib().orc_indexer_head(_ptr(x), _ptr(cs_row), float(np.float32(eps)),
+                           float(np.float32(softmax_scale)), float(np.float32(head_scale)),
+                           float(np.float32(w)), _ptr(codes), _ptr(wo), _ptr(qs))
+    return codes, wo[0], qs[0]
+
+
+def indexer_q_rope_quant(q_bits, positions, cos_sin_cache, weights, softmax_scale,
+                         head_scale=1.0, eps=1e-10):
+    """Oracle indexer path: q_bits uint16 [N, H, 128], weights f32 [N, H] ->
+    (q_fp8 uint8 [N, H, 128], weights_out f32 [N, H])."""
+    q_bits = _need(q_bits, np.uint16, "q")
+    positions = _need(positions, np.int64, "positions")
+    cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
+    weights = _need(weights, np.float32, "weights")
+    N, H, D = q_bits.shape
+    assert D == 128 and weights.shape == (N, H)
+    out = np.zeros((N, H, 128), dtype=np.uint8)
+    wo = np.zeros((N, H), dtype=np.float32)
+    rc = lib().orc_indexer_q_rope_quant(_ptr(q_bits), H * 128, 128, _ptr(positions),
+                                        _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                        _ptr(weights), H, N, H, softmax_scale, head_scale, eps,
+                                        _ptr(out), H * 128, 128, _ptr(wo), H)
+    _check(rc, "indexer_q_rope_quant")
+    return out, wo

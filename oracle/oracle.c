@@ -424,3 +424,86 @@ void orc_pow2_ceil_exp_n(const float* t, int32_t* k, int64_t n) {
   int64_t i;
   for (i = 0; i < n; ++i) k[i] = orc_pow2_ceil_exp(t[i]);
 }
+
+/* ------------------------------------------------ indexer_q_rope_quant */
+
+/* One 128-dim indexer query head ([P5] section 1):
+ *   dims 0..63 get rotate-half ("NeoX") RoPE with pairs (i, i+32), i < 32,
+ *   c = row[i], s = row[32+i]:
+ *     r0 = x_i * c - x_{i+32} * s,   r1 = x_{i+32} * c + x_i * s
+ *   and each rotated value is rounded to bf16 and back (as printed on the
+ *   page for r0; r1 by the same rule); dims 64..127 pass through.
+ *   m = max(max |y|, eps); t = m / 448; q_scale = 2^k with k the exact
+ *   ceiling of log2 t ([P5] section 1: exp2(ceil(log2(amax / 448))));
+ *   codes = e4m3_rne(clamp(y * 2^-k, +-448)) (the scaling is exact);
+ *   w_out = ((w * q_scale) * softmax_scale) * head_scale, left to right as
+ *   printed.  Readings: eps is an argument (the page reports a 1e-4 vs 1e-10
+ *   discussion); head_scale, undefined on the page, is an argument. */
+void orc_indexer_rope(const float* x, const float* cs_row, float* y) {
+  int i;
+  for (i = 0; i < 128; ++i) y[i] = x[i];
+  for (i = 0; i < 32; ++i) {
+    float c = cs_row[i], s = cs_row[32 + i];
+    float x0 = x[i], x1 = x[i + 32];
+    float a = x0 * c, b = x1 * s, d = x1 * c, e = x0 * s;
+    y[i] = orc_bf16_to_f32(orc_f32_to_bf16(a - b));
+    y[i + 32] = orc_bf16_to_f32(orc_f32_to_bf16(d + e));
+  }
+}
+
+void orc_indexer_head(const float* x, const float* cs_row, float eps, float softmax_scale,
+                      float head_scale, float w, uint8_t* codes, float* w_out, float* q_scale) {
+  float y[128];
+  float m = 0.0f;
+  int i, k;
+  orc_indexer_rope(x, cs_row, y);
+  for (i = 0; i < 128; ++i) {
+    float av = fabsf(y[i]);
+    if (av > m) m = av;
+  }
+  if (eps > m) m = eps;
+  k = orc_pow2_ceil_exp(m / E4M3_MAX);
+  for (i = 0; i < 128; ++i) {
+    float v = y[i] * ldexpf(1.0f, -k);
+    if (v > E4M3_MAX) v = E4M3_MAX;
+    if (v < -E4M3_MAX) v = -E4M3_MAX;
+    codes[i] = orc_f32_to_e4m3(v);
+  }
+  *q_scale = ldexpf(1.0f, k);
+  *w_out = ((w * *q_scale) * softmax_scale) * head_scale;
+}
+
+/* q[N, H, 128] bf16 -> q_fp8[N, H, 128] e4m3 (+ folded weights [N, H] fp32).
+ * Strides: q in elements (token, head); q_fp8 in bytes (token, head); weights
+ * and weights_out in elements per token (heads contiguous). */
+int orc_indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,
+                             const int64_t* positions, const float* cos_sin_cache,
+                             int64_t max_pos, const float* weights, int64_t w_stride_token,
+                             int64_t n_tokens, int32_t n_heads, double softmax_scale,
+                             double head_scale, double eps, uint8_t* q_fp8,
+                             int64_t out_stride_token, int64_t out_stride_head,
+                             float* weights_out, int64_t wo_stride_token) {
+  int64_t t;
+  int32_t h;
+  int d;
+  float x[128], qs;
+  if (n_tokens < 0 || n_heads <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
+  if (!eps_ok(eps) || !isfinite(softmax_scale) || !isfinite(head_scale)) return ORC_ERR_VALUE;
+  if (n_tokens == 0) return ORC_OK;
+  if (!q || !positions || !cos_sin_cache || !weights || !q_fp8 || !weights_out)
+    return ORC_ERR_NULL;
+  for (t = 0; t < n_tokens; ++t)
+    if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ERR_VALUE;
+  for (t = 0; t < n_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * ROPE_DIM;
+    for (h = 0; h < n_heads; ++h) {
+      const uint16_t* src = q + t * q_stride_token + (int64_t)h * q_stride_head;
+      for (d = 0; d < 128; ++d) x[d] = orc_bf16_to_f32(src[d]);
+      orc_indexer_head(x, row, (float)eps, (float)softmax_scale, (float)head_scale,
+                       weights[t * w_stride_token + h],
+                       q_fp8 + t * out_stride_token + (int64_t)h * out_stride_head,
+                       &weights_out[t * wo_stride_token + h], &qs);
+    }
+  }
+  return ORC_OK;
+}

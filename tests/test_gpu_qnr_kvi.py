@@ -170,3 +170,56 @@ def test_kvi_bad_position_poisons_its_record():
     assert np.isnan(g[off + 512:off + 528].view(np.float32)).all()  # NaN scales
     g[off:off + 528] = 0xAA
     assert (got == exp).all()
+
+
+# ------------------------------------------------------------- HIP graphs
+
+def test_graph_replays_match_eager_results():
+    # All three ops captured in one HIP graph, replayed several times with the
+    # program's own eager work and synchronizations in between; every replay
+    # must reproduce the eager outputs bit for bit.
+    o, pos, cache = synth.irq_inputs(dict(synth.IRQ_TINY, N=24, H=32, hpg=8, seed=90))
+    qc = dict(synth.QNR_FORWARD, N=24, Hq=8, Hpad=12, seed=91)
+    q, w, qpos, qcache = synth.qnr_inputs(qc)
+    kv = synth.normal_bf16((24, 512), 92, synth.T_KV)
+    slots = synth.slot_permutation(24, 64, 92)
+    od, pd, cd = dev(o), dev(pos), dev(cache)
+    qd, wd, qpd, qcd = dev(q), dev(w), dev(qpos), dev(qcache)
+    kd, sd = dev(kv), dev(slots)
+    out, sc = rq.empty_inv_rope_fp8_quant_outputs(24, 32, 8, DEV)
+    q_out = torch.empty((24, 12, 512), dtype=torch.bfloat16, device=DEV)
+    k_cache = rq.empty_kv_cache(4, 16, DEV, fill=0xAA)
+
+    def step():
+        rq.inv_rope_fp8_quant(od, pd, cd, 8, out, sc)
+        rq.qnorm_rope(qd, wd, qpd, qcd, q_out, 1e-6)
+        rq.kv_rope_quant_insert(kd, qpd, qcd, sd, k_cache, 16)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [host(t).copy() for t in (out, sc, q_out, k_cache)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (out, q_out, k_cache):  # eager work between replays
+            t.view(torch.uint8).fill_(0x5A) if t.dtype != torch.uint8 else t.fill_(0x5A)
+        sc.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp, name in zip((out, sc, q_out, k_cache), eager, ("codes", "scales", "q_out",
+                                                                    "k_cache")):
+            g_bits = host(got)
+            if name == "k_cache":  # bytes outside the records were refilled with 0x5A
+                rec = np.zeros(exp.size, bool)
+                for sl in slots:
+                    off = (sl // 16) * 16 * 528 + (sl % 16) * 528
+                    rec[off:off + 528] = True
+                rec = rec.reshape(exp.shape)
+                assert (g_bits[~rec] == 0x5A).all()
+                g_bits = np.where(rec, g_bits, 0xAA).astype(np.uint8)
+            assert_bits_equal(g_bits, exp, f"replay {rep} {name}")
