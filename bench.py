@@ -37,6 +37,8 @@ KERNEL_SRC = os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", "ropequant.hip")
 #     write; per token 8 + 256 B; plus the 1024 B weight once.
 #   kv_rope_quant_insert per token: 1024 B read + 528 B record + 8 B slot
 #     + 8 + 256 B.
+#   indexer_q_rope_quant per (token, head): 256 B read + 128 B codes + 8 B of
+#     weights; per token 8 + 256 B.
 
 
 def irq_bytes(N, H, fmt="fp32"):
@@ -49,6 +51,12 @@ def qnr_bytes(N, Hq, Hpad):
 
 def kvi_bytes(N):
     return N * (1024 + 528 + 8 + 264)
+
+
+def idx_bytes(N, H):
+    # per (token, head): 256 B bf16 read + 128 B codes + 4 B weight in + 4 B out;
+    # per token: 8 B position + 256 B cos/sin row
+    return N * H * (256 + 128 + 4 + 4) + N * (8 + 256)
 
 
 def kernel_hash():
@@ -125,6 +133,21 @@ def bench_qnr_kvi(args, device, stream):
             args.steps, args.warmup, stream)
         b = kvi_bytes(cfg["N"])
         res["kv_rope_quant_insert"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
+                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+    if args.only in (None, "idx"):
+        N, H = 4096, 64
+        q = synth.normal_bf16((N, H, 128), 55, synth.T_Q)
+        w = np.random.default_rng([55, 9]).uniform(0, 1, (N, H)).astype(np.float32)
+        qd, wd = to_dev(q, device), to_dev(w, device)
+        pd = to_dev(np.arange(N, dtype=np.int64), device)
+        cd = to_dev(synth.cos_sin_cache(N), device)
+        q_fp8 = torch.empty((N, H, 128), dtype=torch.uint8, device=device)
+        wo = torch.empty((N, H), dtype=torch.float32, device=device)
+        ms = time_launches(
+            lambda: rq.indexer_q_rope_quant(qd, pd, cd, wd, q_fp8, wo, 128 ** -0.5),
+            args.steps, args.warmup, stream)
+        b = idx_bytes(N, H)
+        res["indexer_q_rope_quant"] = dict(workload="idx_n4096_h64_d128", us=ms * 1e3, bytes=b,
                                            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
     return res
 
@@ -237,7 +260,8 @@ def main():
     # from idle, so the timed region starts after 100 untimed launches
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "decode", "copy"], default=None)
+    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "decode", "copy"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -256,7 +280,7 @@ def main():
     if args.only == "copy":
         print(json.dumps({"copy_calibration": bench_copy(args, device, stream)}))
         return
-    if args.only in ("qnr", "kvi"):
+    if args.only in ("qnr", "kvi", "idx"):
         print(json.dumps({"extra": bench_qnr_kvi(args, device, stream)}))
         return
     if args.only == "decode":

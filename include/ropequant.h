@@ -17,7 +17,9 @@
  *        wo_a group, scale column = head_in_group * 4 + block), section 2 (the
  *        GPT-J inverse rotation), section 3 (block-128 amax, UE8M0 packing).
  *   [P5] "vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput
- *        향상" (analysis of vLLM PR #46862): section 1 (power-of-two scale).
+ *        향상" (analysis of vLLM PR #46862): section 1 (the fused indexer
+ *        query kernel: rotate-half RoPE with a bf16 round trip, power-of-two
+ *        scale, weight fold).
  *
  * Common conventions
  *   - Head vectors are 512 dims: dims 0..447 are not rotated, dims 448..511
@@ -162,6 +164,35 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
                          uint8_t* k_cache, int64_t num_blocks, int64_t block_stride_bytes,
                          int32_t cache_block_size, int32_t scale_fmt, double eps,
                          void* stream);
+
+/*
+ * indexer_q_rope_quant - the sparse-attention indexer's query path ([P5]
+ * section 1): rotate-half RoPE, per-head power-of-two FP8 quantization, and
+ * the scale folded into the per-head weights.  For t < n_tokens, h < n_heads
+ * (128-dim heads):
+ *   x   = fp32(q[t, h, :])
+ *   for i < 32, c = cos_sin_cache[positions[t], i], s = ... [32 + i]:
+ *     y_i = bf16_round(x_i * c - x_{i+32} * s)
+ *     y_{i+32} = bf16_round(x_{i+32} * c + x_i * s)
+ *   y_d = x_d for d = 64..127; bf16_round = round to bf16 (RNE) and back
+ *   m   = max(max_d |y_d|, eps);  k = smallest integer with 2^k >= m / 448
+ *   q_fp8[t, h, :]     = e4m3_rne(y * 2^-k)
+ *   weights_out[t, h]  = ((weights[t, h] * 2^k) * softmax_scale) * head_scale
+ * q: bf16 [N, H, 128], strides (q_stride_token, q_stride_head, 1), base
+ *   16-byte aligned, strides multiples of 8.  weights / weights_out: fp32
+ *   [N, H] with token strides w_stride_token / wo_stride_token (heads
+ *   contiguous); weights_out may be weights itself (in place).  q_fp8: e4m3
+ *   [N, H, 128] with byte strides (out_stride_token, out_stride_head), 8-byte
+ *   aligned, multiples of 8, rows not overlapping.  softmax_scale, head_scale
+ *   finite (as fp32); eps >= 2^-116 as fp32.  n_tokens * n_heads < 2^31.
+ *   A head whose position is out of range gets a NaN weight.
+ */
+int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,
+                         const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                         const float* weights, int64_t w_stride_token, int64_t n_tokens,
+                         int32_t n_heads, double softmax_scale, double head_scale, double eps,
+                         uint8_t* q_fp8, int64_t out_stride_token, int64_t out_stride_head,
+                         float* weights_out, int64_t wo_stride_token, void* stream);
 
 /*
  * Launch-shape knob (process-wide, thread-safe): 0 lets the launch table pick

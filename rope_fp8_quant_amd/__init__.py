@@ -12,14 +12,16 @@ Sources: the op semantics follow the analyses of vLLM PR #63540
 ("한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE + FP8 quant
 커널 3.5배 가속기", sections 1-3) for ``inv_rope_fp8_quant`` and of vLLM PR
 #49236 ("vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선",
-sections 1-2) for ``qnorm_rope`` and ``kv_rope_quant_insert``.
+sections 1-2) for ``qnorm_rope`` and ``kv_rope_quant_insert``, and of vLLM PR
+#46862 ("vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput 향상",
+section 1) for ``indexer_q_rope_quant``.
 """
 import torch
 
 from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, lib
 
 __all__ = [
-    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
+    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert", "indexer_q_rope_quant",
     "empty_inv_rope_fp8_quant_outputs", "empty_kv_cache", "set_block_threads",
     "abi_version", "RopeQuantError", "RECORD_BYTES", "SCALE_FMTS",
 ]
@@ -187,3 +189,32 @@ def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, ca
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, k_cache.data_ptr(), k_cache.shape[0],
         k_cache.stride(0), bs, fmt, float(eps), _stream(kv.device, stream))
     check("kv_rope_quant_insert", rc)
+
+
+def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_out,
+                         softmax_scale, head_scale=1.0, eps=1e-10, stream=None):
+    """Indexer query path: rotate-half RoPE on dims 0..63 of q [N, H, 128] bf16
+    (rotated values rounded through bf16), per-head power-of-two e4m3
+    quantization into q_fp8 [N, H, 128] (uint8 / float8_e4m3fn), and the scale
+    folded into weights_out[N, H] = ((weights * q_scale) * softmax_scale) *
+    head_scale (float32; may be ``weights`` itself)."""
+    _cuda(q, "q")
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 128 or q.stride(2) != 1:
+        raise ValueError("q must be bf16 [N, H, 128] with a contiguous last dim")
+    N, H, _ = q.shape
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    for t, name in ((weights, "weights"), (weights_out, "weights_out")):
+        if (t.dtype != torch.float32 or tuple(t.shape) != (N, H)
+                or (H > 1 and t.stride(1) != 1)):
+            raise ValueError(f"{name} must be float32 [N, H] with contiguous heads")
+    if q_fp8.dtype not in _BYTE_DTYPES or tuple(q_fp8.shape) != (N, H, 128) or (
+            q_fp8.stride(2) != 1):
+        raise ValueError("q_fp8 must be uint8/float8_e4m3fn [N, H, 128], last dim contiguous")
+    _same_device(q, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                 (weights, "weights"), (q_fp8, "q_fp8"), (weights_out, "weights_out"))
+    rc = lib().indexer_q_rope_quant(
+        q.data_ptr(), q.stride(0), q.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0], weights.data_ptr(), weights.stride(0), N, H,
+        float(softmax_scale), float(head_scale), float(eps), q_fp8.data_ptr(), q_fp8.stride(0),
+        q_fp8.stride(1), weights_out.data_ptr(), weights_out.stride(0), _stream(q.device, stream))
+    check("indexer_q_rope_quant", rc)

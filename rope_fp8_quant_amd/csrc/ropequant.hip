@@ -613,6 +613,146 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   }
 }
 
+// ---------------------------------------------------- indexer query path
+
+// One 128-dim indexer head per 16-lane row, lane L holding dims [8L, 8L+8)
+// as one 16-byte load, so a wave's load instruction reads 4 whole heads
+// (1 KiB, contiguous when heads are).  A wave takes 4 * kIdxRounds heads in
+// kIdxRounds rounds and issues all rounds' reads first.  Rotate-half pairs (i, i+32) sit 4 lanes
+// apart (lanes 0..3 hold dims 0..31, lanes 4..7 dims 32..63): two DPP row
+// shifts bring each lane its partner's 8 values.
+struct IdxParams {
+  LaunchHdr hdr;
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  const int64_t* positions;
+  const float* cs;
+  int64_t max_pos;
+  const float* w;
+  int64_t w_st;
+  uint32_t units;  // n_tokens * n_heads
+  Magic div_heads;
+  uint32_t n_heads;
+  float softmax_scale, head_scale, eps;
+  uint8_t* out;
+  int64_t out_st, out_sh;
+  float* wo;
+  int64_t wo_st;
+};
+
+constexpr int kRowShl4 = 0x104;  // lane i <- lane i+4 within the row
+constexpr int kRowShr4 = 0x114;  // lane i <- lane i-4 within the row
+constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 4)
+
+__global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, L = lane & 15;
+  const uint32_t unit0 = wave_index(p.hdr) * (4u * kIdxRounds);
+  uint4 raw[kIdxRounds];
+  uint32_t tj[kIdxRounds], hj[kIdxRounds];
+  const uint4* rowp[kIdxRounds];
+#pragma unroll
+  for (int j = 0; j < kIdxRounds; ++j) {
+    // (a tail wave repeats the last unit; units past the end store nothing)
+    const uint32_t u = min(unit0 + 4u * j + q, p.units - 1u);
+    tj[j] = magic_div(u, p.div_heads);
+    hj[j] = u - tj[j] * p.n_heads;
+    rowp[j] = reinterpret_cast<const uint4*>(p.q + (int64_t)tj[j] * p.q_st +
+                                             (int64_t)hj[j] * p.q_sh) + L;
+  }
+  int64_t pos[kIdxRounds];
+#pragma unroll
+  for (int j = 0; j < kIdxRounds; ++j) pos[j] = p.positions[tj[j]];
+#pragma unroll
+  for (int j = 0; j < kIdxRounds; ++j) raw[j] = load_nt(rowp[j]);
+  // cos/sin for this lane's 8 frequencies i = 8(L & 3) + e, and the weight
+  float4 cv[kIdxRounds][2], sv[kIdxRounds][2];
+  float wgt[kIdxRounds];
+  bool badj[kIdxRounds];
+#pragma unroll
+  for (int j = 0; j < kIdxRounds; ++j) {
+    badj[j] = pos[j] < 0 || pos[j] >= p.max_pos;
+    const float4* row = reinterpret_cast<const float4*>(p.cs + (badj[j] ? 0 : pos[j]) * 64);
+    cv[j][0] = row[2 * (L & 3)];
+    cv[j][1] = row[2 * (L & 3) + 1];
+    sv[j][0] = row[8 + 2 * (L & 3)];
+    sv[j][1] = row[8 + 2 * (L & 3) + 1];
+    wgt[j] = p.w[(int64_t)tj[j] * p.w_st + hj[j]];
+  }
+
+#pragma unroll
+  for (int j = 0; j < kIdxRounds; ++j) {
+    // partner dwords: lanes 0..3 take lane L+4's, lanes 4..7 lane L-4's
+    const uint32_t own[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+    uint32_t par[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t up = dpp_u32<kRowShl4>(own[i]);
+      const uint32_t dn = dpp_u32<kRowShr4>(own[i]);
+      par[i] = (L & 4) ? dn : up;
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf_lo(own[i]);
+      x[2 * i + 1] = bf_hi(own[i]);
+    }
+    if (L < 8) {
+      // r0 = x_i c - x_{i+32} s (lanes 0..3), r1 = x_{i+32} c + x_i s (lanes
+      // 4..7): own * c + partner * s', with s' = -s on lanes 0..3 (negating
+      // a rounded product is exact), then rounded to bf16 and back
+      const float c8[8] = {cv[j][0].x, cv[j][0].y, cv[j][0].z, cv[j][0].w,
+                           cv[j][1].x, cv[j][1].y, cv[j][1].z, cv[j][1].w};
+      const float s8[8] = {sv[j][0].x, sv[j][0].y, sv[j][0].z, sv[j][0].w,
+                           sv[j][1].x, sv[j][1].y, sv[j][1].z, sv[j][1].w};
+      const bool first = L < 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = bf_lo(par[i]), p1 = bf_hi(par[i]);
+        const float s0 = first ? -s8[2 * i] : s8[2 * i];
+        const float s1 = first ? -s8[2 * i + 1] : s8[2 * i + 1];
+        const float y0 = x[2 * i] * c8[2 * i] + p0 * s0;
+        const float y1 = x[2 * i + 1] * c8[2 * i + 1] + p1 * s1;
+        x[2 * i] = (float)(__bf16)y0;
+        x[2 * i + 1] = (float)(__bf16)y1;
+      }
+    }
+    // per-head amax over the row, power-of-two scale ([P5] section 1)
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
+    m = __builtin_fmaxf(m, dpp_f32<kQuadSwap1>(m));
+    m = __builtin_fmaxf(m, dpp_f32<kQuadSwap2>(m));
+    m = __builtin_fmaxf(m, dpp_f32<kRowHalfMirror>(m));
+    m = __builtin_fmaxf(m, dpp_f32<kRowMirror>(m));
+    m = __builtin_fmaxf(m, p.eps);
+    const uint32_t tb = __builtin_bit_cast(uint32_t, m / kE4m3Max);
+    const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
+    const float qs = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
+    const float mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
+    // |x * mult| <= 448 (1 + 2^-24) < 464: the convert needs no clamp
+    uint32_t code[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float a0 = x[4 * h] * mult, a1 = x[4 * h + 1] * mult;
+      const float a2 = x[4 * h + 2] * mult, a3 = x[4 * h + 3] * mult;
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __builtin_bit_cast(int, a0), false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, wd, true);
+      code[h] = (uint32_t)wd;
+    }
+    if (unit0 + 4u * j + q < p.units) {
+      *reinterpret_cast<uint2*>(p.out + (int64_t)tj[j] * p.out_st + (int64_t)hj[j] * p.out_sh +
+                                8 * L) = make_uint2(code[0], code[1]);
+      if (L == 0) {
+        // fold the scale into the weight, left to right as printed; a head
+        // whose position is outside the table gets a NaN weight
+        const float fold = ((wgt[j] * qs) * p.softmax_scale) * p.head_scale;
+        p.wo[(int64_t)tj[j] * p.wo_st + hj[j]] = badj[j] ? __builtin_nanf("") : fold;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ host side
 
 std::atomic<int> g_block_threads{0};  // 0: launch table decides
@@ -666,7 +806,7 @@ bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
 
 // Every params struct starts with a LaunchHdr, filled in here.
 int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
-           hipStream_t stream) {
+           hipStream_t stream, bool uses_lds = true) {
   const int threads = pick_block_threads(units);
   LaunchHdr* hdr = static_cast<LaunchHdr*>(params);
   hdr->wpb_log2 = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
@@ -674,7 +814,7 @@ int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
   const uint32_t per_block = (uint32_t)threads / 16u;
   const uint32_t blocks = (units + per_block - 1) / per_block;
   void* args[] = {params};
-  const size_t lds_bytes = (size_t)(threads / 64) * 4096;  // 4 KiB staging per wave
+  const size_t lds_bytes = uses_lds ? (size_t)(threads / 64) * 4096 : 0;  // 4 KiB per wave
   const hipError_t e =
       hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, lds_bytes, stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
@@ -684,6 +824,12 @@ int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
 constexpr uint32_t kIrqChunkLog2 = 6;
 constexpr uint32_t kQnrChunkLog2 = 4;
 constexpr uint32_t kKviChunkLog2 = 4;
+constexpr uint32_t kIdxChunkLog2 = 4;
+
+bool finite_f32(double v) {
+  const float f = (float)v;
+  return v == v && f == f && f - f == 0.0f;
+}
 
 }  // namespace
 
@@ -810,6 +956,46 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)kvi_kernel<RQ_SCALE_FP32>;
   return launch(fn, p.n_tokens, kKviChunkLog2, &p, (hipStream_t)stream);
+}
+
+int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,
+                         const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                         const float* weights, int64_t w_stride_token, int64_t n_tokens,
+                         int32_t n_heads, double softmax_scale, double head_scale, double eps,
+                         uint8_t* q_fp8, int64_t out_stride_token, int64_t out_stride_head,
+                         float* weights_out, int64_t wo_stride_token, void* stream) {
+  if (n_tokens < 0 || n_heads < 1 || max_pos < 1) return RQ_ERR_SHAPE;
+  if ((int64_t)n_tokens * n_heads >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
+  if (!eps_quant_ok(eps) || !finite_f32(softmax_scale) || !finite_f32(head_scale))
+    return RQ_ERR_VALUE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!q || !positions || !cos_sin_cache || !weights || !q_fp8 || !weights_out)
+    return RQ_ERR_NULL;
+  if (q_stride_token < 1 || q_stride_head < 1 || w_stride_token < 1 || out_stride_token < 1 ||
+      out_stride_head < 1 || wo_stride_token < 1)
+    return RQ_ERR_STRIDE;
+  if (!aligned(q, 16) || (q_stride_token % 8) || (q_stride_head % 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin_cache, 16) || !aligned(weights, 4) || !aligned(q_fp8, 8) ||
+      (out_stride_token % 8) || (out_stride_head % 8) || !aligned(weights_out, 4))
+    return RQ_ERR_ALIGN;
+  {
+    const int64_t n[2] = {n_tokens, n_heads}, st[2] = {out_stride_token, out_stride_head};
+    if (!no_overlap(2, n, st, 128)) return RQ_ERR_STRIDE;
+    const int64_t sw[2] = {wo_stride_token, 1};
+    if (!no_overlap(2, n, sw, 1)) return RQ_ERR_STRIDE;
+  }
+  IdxParams p;
+  p.q = q; p.q_st = q_stride_token; p.q_sh = q_stride_head;
+  p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
+  p.w = weights; p.w_st = w_stride_token;
+  p.units = (uint32_t)(n_tokens * n_heads);
+  p.div_heads = make_magic((uint32_t)n_heads); p.n_heads = (uint32_t)n_heads;
+  p.softmax_scale = (float)softmax_scale; p.head_scale = (float)head_scale; p.eps = (float)eps;
+  p.out = q_fp8; p.out_st = out_stride_token; p.out_sh = out_stride_head;
+  p.wo = weights_out; p.wo_st = wo_stride_token;
+  // 4 * kIdxRounds heads per wave: size the launch in rows of kIdxRounds heads
+  const uint32_t rows = (p.units + kIdxRounds - 1) / kIdxRounds;
+  return launch((const void*)idx_kernel, rows, kIdxChunkLog2, &p, (hipStream_t)stream, false);
 }
 
 }  // extern "C"

@@ -154,6 +154,35 @@ def test_kvi_validation(kw, status):
     assert kvi(**kw) == status
 
 
+def idx(**kw):
+    a = dict(q=A, qst=64 * 128, qsh=128, pos=A, cs=A, max_pos=4096, w=A, wst=64, n=8, h=64,
+             ss=128 ** -0.5, hs=1.0, eps=1e-10, out=A, ost=64 * 128, osh=128, wo=A, wost=64)
+    a.update(kw)
+    return _lib.lib().indexer_q_rope_quant(a["q"], a["qst"], a["qsh"], a["pos"], a["cs"],
+                                           a["max_pos"], a["w"], a["wst"], a["n"], a["h"],
+                                           a["ss"], a["hs"], a["eps"], a["out"], a["ost"],
+                                           a["osh"], a["wo"], a["wost"], None)
+
+
+def test_indexer_zero_tokens_is_ok_without_pointers():
+    assert idx(n=0, q=None, pos=None, cs=None, w=None, out=None, wo=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=0), SHAPE), (dict(n=-1), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(n=1 << 25, h=64), SHAPE),
+    (dict(eps=0.0), VALUE), (dict(ss=float("inf")), VALUE), (dict(hs=float("nan")), VALUE),
+    (dict(ss=1e300), VALUE),
+    (dict(q=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL), (dict(wo=None), NULL),
+    (dict(qst=0), STRIDE), (dict(wost=0), STRIDE), (dict(osh=64), STRIDE), (dict(wost=32), STRIDE),
+    (dict(q=A + 8), ALIGN), (dict(qsh=132), ALIGN), (dict(out=A + 4), ALIGN),
+    (dict(osh=132), ALIGN), (dict(w=A + 2), ALIGN), (dict(cs=A + 4), ALIGN),
+])
+def test_indexer_validation(kw, status):
+    assert idx(**kw) == status
+
+
 def test_python_binding_rejects_host_tensors():
     import rope_fp8_quant_amd as rq
     o = torch.zeros((2, 8, 512), dtype=torch.bfloat16)

@@ -1,0 +1,113 @@
+"""GPU parity of indexer_q_rope_quant (HIP path through the C ABI) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_fp8_quant_amd as rq
+from rope_fp8_quant_amd import synth
+from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SOFTMAX_SCALE = 128 ** -0.5
+
+
+@pytest.fixture(autouse=True)
+def _table_launch():
+    rq.set_block_threads(0)
+    yield
+    rq.set_block_threads(0)
+
+
+def idx_inputs(N, H, seed, max_pos=4096, pos=None):
+    q = synth.normal_bf16((N, H, 128), seed, synth.T_Q)
+    w = np.random.default_rng([seed, 9]).uniform(0, 1, (N, H)).astype(np.float32)
+    if pos is None:
+        pos = synth.uniform_positions(N, max_pos, seed)
+    return q, w, pos, synth.cos_sin_cache(max_pos)
+
+
+def idx_gpu(q, w, pos, cache, head_scale=1.0, eps=1e-10, q_dev=None, inplace=False):
+    N, H, _ = q.shape
+    q_fp8 = torch.full((N, H, 128), 0xCD, dtype=torch.uint8, device=DEV)
+    wd = dev(w)
+    wo = wd if inplace else torch.full((N, H), -3.0, dtype=torch.float32, device=DEV)
+    rq.indexer_q_rope_quant(dev(q) if q_dev is None else q_dev, dev(pos), dev(cache), wd, q_fp8,
+                            wo, SOFTMAX_SCALE, head_scale, eps)
+    torch.cuda.synchronize()
+    return host(q_fp8), host(wo)
+
+
+def idx_check(q, w, pos, cache, what, head_scale=1.0, eps=1e-10, **kw):
+    print(f"[case] indexer {what} N={q.shape[0]} H={q.shape[1]}", flush=True)
+    got, gw = idx_gpu(q, w, pos, cache, head_scale, eps, **kw)
+    exp, ew = oracle.indexer_q_rope_quant(q, pos, cache, w, SOFTMAX_SCALE, head_scale, eps)
+    assert_bits_equal(gw, ew, f"indexer {what} weights")
+    assert_codes_match(got, exp, f"indexer {what} codes")
+
+
+def test_indexer_full_size():
+    # 4096 tokens x 64 heads x 128 dims, weights ~U(0,1), softmax scale 128^-0.5
+    idx_check(*idx_inputs(4096, 64, 55, max_pos=4096, pos=np.arange(4096, dtype=np.int64)),
+              "4096x64x128")
+
+
+@pytest.mark.parametrize("threads", [64, 256])
+def test_indexer_ragged(threads):
+    rq.set_block_threads(threads)
+    idx_check(*idx_inputs(37, 5, 56, max_pos=65536), f"ragged threads={threads}")
+
+
+@pytest.mark.parametrize("N", synth.DECODE_NS)
+def test_indexer_decode_sizes(N):
+    idx_check(*idx_inputs(N, 64, 60 + N, max_pos=65536), "decode", head_scale=0.75)
+
+
+def test_indexer_strided_input_and_in_place_weights():
+    q, w, pos, cache = idx_inputs(19, 12, 57)
+    big = torch.zeros((19, 12, 384), dtype=torch.bfloat16, device=DEV)
+    big[:, :, 128:256] = dev(q)
+    print("[case] indexer strided + in-place", flush=True)
+    got, gw = idx_gpu(q, w, pos, cache, q_dev=big[:, :, 128:256], inplace=True)
+    exp, ew = oracle.indexer_q_rope_quant(q, pos, cache, w, SOFTMAX_SCALE)
+    assert_bits_equal(gw, ew, "in-place weights")
+    assert_codes_match(got, exp, "strided codes")
+
+
+def test_indexer_degenerate_heads():
+    rng = np.random.default_rng(58)
+    q = np.zeros((4, 8, 128), np.uint16)
+    q[0, 1] = 0x8000
+    q[1, 0] = synth.f32_to_bf16_bits(np.full(128, -2.5, np.float32))
+    q[1, 2] = synth.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e20)
+    q[2, 3] = synth.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e-20)
+    q[2, 4] = rng.integers(1, 0x80, size=128).astype(np.uint16)  # bf16 subnormals
+    q[3] = synth.f32_to_bf16_bits(rng.standard_normal((8, 128)).astype(np.float32))
+    q[3, 5, :64] = 0
+    w = rng.uniform(0, 1, (4, 8)).astype(np.float32)
+    pos = np.array([0, 3, 1000, 4095], np.int64)
+    for eps in (1e-10, 1e-4):
+        idx_check(q, w, pos, synth.cos_sin_cache(4096), f"degenerate eps={eps}", eps=eps)
+
+
+def test_indexer_bad_position_gives_nan_weight():
+    q, w, pos, cache = idx_inputs(6, 4, 59)
+    bad = pos.copy()
+    bad[3] = cache.shape[0]
+    got, gw = idx_gpu(q, w, bad, cache)
+    good = [0, 1, 2, 4, 5]
+    exp, ew = oracle.indexer_q_rope_quant(q[good].copy(), pos[good].copy(), cache,
+                                          w[good].copy(), SOFTMAX_SCALE)
+    assert (got[good] == exp).all() and (gw[good] == ew).all()
+    assert np.isnan(gw[3]).all()
+
+
+def test_indexer_launch_shapes_bit_identical():
+    q, w, pos, cache = idx_inputs(301, 64, 61, max_pos=65536)
+    res = []
+    for threads in (64, 128, 256):
+        rq.set_block_threads(threads)
+        res.append(idx_gpu(q, w, pos, cache))
+    for got, gw in res[1:]:
+        assert (got == res[0][0]).all() and (gw.view(np.uint32) == res[0][1].view(np.uint32)).all()
