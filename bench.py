@@ -134,6 +134,21 @@ def bench_qnr_kvi(args, device, stream):
         b = kvi_bytes(cfg["N"])
         res["kv_rope_quant_insert"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
                                            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+        # the same q and kv work in one launch (positions 0..8191 serve both)
+        qc = synth.QNR_FORWARD
+        q, w, qpos, qcache = synth.qnr_inputs(qc)
+        qd, wd = to_dev(q, device), to_dev(w, device)
+        del q
+        q_out = torch.empty((qc["N"], qc["Hpad"], 512), dtype=torch.bfloat16, device=device)
+        ms = time_launches(
+            lambda: rq.qnorm_rope_kv_rope_quant_insert(qd, wd, kd, pd, cd, sd, q_out, k_cache,
+                                                       cfg["block_size"], qc["eps"]),
+            args.steps, args.warmup, stream)
+        b = qnr_bytes(qc["N"], qc["Hq"], qc["Hpad"]) + kvi_bytes(cfg["N"]) - cfg["N"] * 264
+        res["qnorm_rope_kv_rope_quant_insert"] = dict(
+            workload="qnr_forward + kvi_forward, one launch", us=ms * 1e3, bytes=b,
+            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+        del qd, q_out
     if args.only in (None, "idx"):
         N, H = 4096, 64
         q = synth.normal_bf16((N, H, 128), 55, synth.T_Q)

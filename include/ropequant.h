@@ -166,6 +166,24 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
                          void* stream);
 
 /*
+ * qnorm_rope_kv_rope_quant_insert - qnorm_rope and kv_rope_quant_insert in a
+ * single launch, the op's own shape in [P1] section 1 (the `_out` form: q_out
+ * and k_cache preallocated by the caller, nothing returned; section 2 gives
+ * the schema).  Every argument means what it means in the two functions
+ * above, the two share positions / cos_sin_cache / n_tokens, and the results
+ * are bit-identical to calling both: eps is the RMSNorm epsilon, quant_eps the
+ * kv amax floor (>= 2^-116 as fp32).  Validation is the union of both.
+ */
+int qnorm_rope_kv_rope_quant_insert(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, uint16_t* q_out, uint8_t* k_cache, int64_t num_blocks,
+    int64_t block_stride_bytes, int32_t cache_block_size, int32_t scale_fmt, double quant_eps,
+    void* stream);
+
+/*
  * indexer_q_rope_quant - the sparse-attention indexer's query path ([P5]
  * section 1): rotate-half RoPE, per-head power-of-two FP8 quantization, and
  * the scale folded into the per-head weights.  For t < n_tokens, h < n_heads

@@ -291,3 +291,14 @@ def indexer_q_rope_quant(q_bits, positions, cos_sin_cache, weights, softmax_scal
                                         _ptr(out), H * 128, 128, _ptr(wo), H)
     _check(rc, "indexer_q_rope_quant")
     return out, wo
+
+
+def qnorm_rope_kv_rope_quant_insert(q_bits, weight_bits, kv_bits, positions, cos_sin_cache,
+                                    slot_mapping, k_cache, q_head_padded, cache_block_size,
+                                    eps=1e-6, scale_fmt=SCALE_FP32, quant_eps=1e-10,
+                                    block_stride_bytes=None):
+    """The fused op is, by definition, both ops on the same positions."""
+    q_out = qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps)
+    kv_rope_quant_insert(kv_bits, positions, cos_sin_cache, slot_mapping, k_cache,
+                         cache_block_size, block_stride_bytes, scale_fmt, quant_eps)
+    return q_out, k_cache

@@ -21,7 +21,8 @@ import torch
 from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, lib
 
 __all__ = [
-    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert", "indexer_q_rope_quant",
+    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
+    "qnorm_rope_kv_rope_quant_insert", "indexer_q_rope_quant",
     "empty_inv_rope_fp8_quant_outputs", "empty_kv_cache", "set_block_threads",
     "abi_version", "RopeQuantError", "RECORD_BYTES", "SCALE_FMTS",
 ]
@@ -134,10 +135,7 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
     check("inv_rope_fp8_quant", rc)
 
 
-def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, stream=None):
-    """Per-head RMSNorm + forward RoPE of q_in [N, Hq, 512] bf16 into the
-    contiguous q_out [N, q_head_padded, 512] bf16; pad heads are zeroed.
-    norm_weight: bf16 [512] or None."""
+def _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out):
     _cuda(q_in, "q_in")
     if q_in.dtype != torch.bfloat16 or q_in.dim() != 3 or q_in.shape[2] != 512 or (
             q_in.stride(2) != 1):
@@ -155,6 +153,33 @@ def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, str
         raise ValueError("norm_weight must be contiguous bf16 [512] or None")
     _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
                  (q_out, "q_out"), (norm_weight, "norm_weight"))
+    return N, Hq
+
+
+def _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size):
+    _cuda(kv, "kv")
+    if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != 512 or kv.stride(1) != 1:
+        raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
+    N = kv.shape[0]
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
+            or not slot_mapping.is_contiguous()):
+        raise ValueError("slot_mapping must be contiguous int64 [N]")
+    if k_cache.dtype != torch.uint8 or k_cache.dim() != 2 or k_cache.stride(1) != 1:
+        raise ValueError("k_cache must be uint8 [num_blocks, block_bytes]")
+    if k_cache.shape[1] < int(cache_block_size) * RECORD_BYTES:
+        raise ValueError("k_cache block_bytes must hold cache_block_size * 528 bytes")
+    _same_device(kv, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                 (slot_mapping, "slot_mapping"), (k_cache, "k_cache"))
+    return N
+
+
+def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, stream=None):
+    """Per-head RMSNorm + forward RoPE of q_in [N, Hq, 512] bf16 into the
+    contiguous q_out [N, q_head_padded, 512] bf16; pad heads are zeroed.
+    norm_weight: bf16 [512] or None.  With q_head_padded == Hq, q_out may be
+    q_in itself (contiguous): each head is read before it is written."""
+    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
     rc = lib().qnorm_rope(
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
@@ -169,26 +194,30 @@ def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, ca
     token's 528-byte record written at its slot of the paged uint8 cache
     k_cache [num_blocks, block_bytes] (block stride = k_cache.stride(0))."""
     fmt = _fmt(scale_fmt)
-    _cuda(kv, "kv")
-    if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != 512 or kv.stride(1) != 1:
-        raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
-    N = kv.shape[0]
-    _check_rope_inputs(positions, cos_sin_cache, N)
-    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
-            or not slot_mapping.is_contiguous()):
-        raise ValueError("slot_mapping must be contiguous int64 [N]")
-    if k_cache.dtype != torch.uint8 or k_cache.dim() != 2 or k_cache.stride(1) != 1:
-        raise ValueError("k_cache must be uint8 [num_blocks, block_bytes]")
-    bs = int(cache_block_size)
-    if k_cache.shape[1] < bs * RECORD_BYTES:
-        raise ValueError("k_cache block_bytes must hold cache_block_size * 528 bytes")
-    _same_device(kv, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
-                 (slot_mapping, "slot_mapping"), (k_cache, "k_cache"))
+    N = _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size)
     rc = lib().kv_rope_quant_insert(
         kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, k_cache.data_ptr(), k_cache.shape[0],
-        k_cache.stride(0), bs, fmt, float(eps), _stream(kv.device, stream))
+        k_cache.stride(0), int(cache_block_size), fmt, float(eps), _stream(kv.device, stream))
     check("kv_rope_quant_insert", rc)
+
+
+def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_cache,
+                                    slot_mapping, q_out, k_cache, cache_block_size, eps=1e-6,
+                                    scale_fmt="fp32", quant_eps=1e-10, stream=None):
+    """qnorm_rope and kv_rope_quant_insert in one launch (same results)."""
+    fmt = _fmt(scale_fmt)
+    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
+    if _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size) != N:
+        raise ValueError("q_in and kv must have the same number of tokens")
+    rc = lib().qnorm_rope_kv_rope_quant_insert(
+        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
+        None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
+        positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+        slot_mapping.data_ptr(), N, Hq, q_out.shape[1], float(eps), q_out.data_ptr(),
+        k_cache.data_ptr(), k_cache.shape[0], k_cache.stride(0), int(cache_block_size), fmt,
+        float(quant_eps), _stream(q_in.device, stream))
+    check("qnorm_rope_kv_rope_quant_insert", rc)
 
 
 def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_out,

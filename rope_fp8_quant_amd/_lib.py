@@ -14,7 +14,8 @@ RQ_OK = 0
 RQ_SCALE_FP32 = 0
 RQ_SCALE_UE8M0 = 1
 
-EXPORTS = ("inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert", "indexer_q_rope_quant",
+EXPORTS = ("inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
+           "qnorm_rope_kv_rope_quant_insert", "indexer_q_rope_quant",
            "ropequant_strerror", "ropequant_abi_version", "ropequant_set_block_threads")
 
 _lock = threading.Lock()
@@ -51,6 +52,10 @@ def lib():
         L.kv_rope_quant_insert.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, I32, I32, D,
                                            P]
         L.kv_rope_quant_insert.restype = I
+        L.qnorm_rope_kv_rope_quant_insert.argtypes = [P, I64, I64, P, P, I64, P, P, I64, P, I64,
+                                                      I32, I32, D, P, P, I64, I64, I32, I32, D,
+                                                      P]
+        L.qnorm_rope_kv_rope_quant_insert.restype = I
         L.indexer_q_rope_quant.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, I32, D, D, D,
                                            P, I64, I64, P, I64, P]
         L.indexer_q_rope_quant.restype = I

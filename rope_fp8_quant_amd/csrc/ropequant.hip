@@ -138,6 +138,14 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Wave-uniform read of an input that no kernel writes while this one runs
+// (token positions, slot ids).  Through the constant address space it is
+// always a scalar load, whatever shape the surrounding control flow takes.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   // LDS operations of one wave complete in issue order; these keep the
   // compiler from moving the reads above the writes.
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     const uint32_t g = magic_div(h, p.div_hpg);
     const uint32_t j = h - g * p.hpg;
     rows[k] = p.o + (int64_t)t * p.o_st + (int64_t)h * p.o_sh;
-    posk[k] = p.positions[t];
+    posk[k] = load_uniform(p.positions + t);
     outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim;
     const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
                           (int64_t)(FMT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
@@ -415,13 +423,12 @@ struct QnrParams {
   uint16_t* q_out;
 };
 
+// The wave with grid-wide index `wave` handles units 4*wave .. 4*wave+3.
 template <bool HAS_WEIGHT>
-__global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
-  extern __shared__ uint4 lds[];
+__device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15;
-  const uint32_t unit0 = wave_index(p.hdr) * 4u;
-  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint32_t unit0 = wave * 4u;
   const uint16_t* rows[4];
   uint32_t livek[4];
   int64_t posk[4];
@@ -432,7 +439,7 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
     const uint32_t h = u - t * p.hpad;
     livek[k] = (unit0 + k < p.units && h < p.hq) ? 1u : 0u;
     rows[k] = p.q + (int64_t)t * p.q_st + (int64_t)min(h, p.hq - 1u) * p.q_sh;
-    posk[k] = p.positions[t];
+    posk[k] = load_uniform(p.positions + t);
   }
   // A wave of pad heads only reads nothing (its rows in LDS are never used).
   uint4 raw[4] = {}, w[4];
@@ -533,6 +540,12 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
           lds_wave[64 * k + rslot];
 }
 
+template <bool HAS_WEIGHT>
+__global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
+  extern __shared__ uint4 lds[];
+  qnr_body<HAS_WEIGHT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
+}
+
 struct KviParams {
   LaunchHdr hdr;
   const uint16_t* kv;
@@ -550,13 +563,12 @@ struct KviParams {
   float eps;
 };
 
+// The wave with grid-wide index `wave` handles tokens 4*wave .. 4*wave+3.
 template <int FMT>
-__global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
-  extern __shared__ uint4 lds[];
+__device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
-  const uint32_t t0 = wave_index(p.hdr) * 4u;
-  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint32_t t0 = wave * 4u;
   const uint16_t* rows[4];
   const float* csk[4];
   int64_t posk[4];
@@ -566,10 +578,10 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t t = min(t0 + k, p.n_tokens - 1u);
-    slotk[k] = p.slots[t];
+    slotk[k] = load_uniform(p.slots + t);
     if (t0 + k >= p.n_tokens) slotk[k] = -1;
     rows[k] = p.kv + (int64_t)t * p.kv_st;
-    posk[k] = p.positions[t];
+    posk[k] = load_uniform(p.positions + t);
   }
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
@@ -589,27 +601,65 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   load_cs(PICK_ROW(q, csk), r, cs);  // unconditional, as above
   transpose_rows(lds_wave, raw, lane, w);
   uint8_t* const rec = PICK_ROW(q, reck);
-  if (!rec) return;  // whole rows only
-  const int d0 = lane_dim0(L);
+  // Rows with nothing to write skip the rest; no early return, so a caller
+  // that inlines this body keeps a plain if/else around it.
+  if (rec) {
+    const int d0 = lane_dim0(L);
 
-  Vals v;
-  unpack_bf16(w, v);
-  if (L >= 12) rope_lane<false>(v, cs);
-  float scale;
-  uint32_t ebyte, codes[8];
-  quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
-  uint32_t word = 0;
-  if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
+    Vals v;
+    unpack_bf16(w, v);
+    if (L >= 12) rope_lane<false>(v, cs);
+    float scale;
+    uint32_t ebyte, codes[8];
+    quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
+    uint32_t word = 0;
+    if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
-  if (r == 0) {
-    // a token whose position is outside the table gets NaN scales
-    const bool bad = PICK_ROW(q, badk) != 0;
-    uint32_t tail;
-    if (FMT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
-    else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
-    *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * blk) = tail;
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
+    if (r == 0) {
+      // a token whose position is outside the table gets NaN scales
+      const bool bad = PICK_ROW(q, badk) != 0;
+      uint32_t tail;
+      if (FMT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
+      else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
+      *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * blk) = tail;
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
+  extern __shared__ uint4 lds[];
+  kvi_body<FMT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
+}
+
+// qnorm_rope and kv_rope_quant_insert in one launch ([P1] section 1: the op
+// normalizes and rotates q and inserts the rotated, quantized kv in a single
+// kernel).  Waves [0, q_waves) run the q path, the rest the kv path; the
+// branch is per wave, and every wave has its own LDS slice.
+struct FusedParams {
+  LaunchHdr hdr;
+  QnrParams q;
+  KviParams k;
+  uint32_t q_waves;
+};
+
+// s_waitcnt vmcnt(0), the other counters left at their maximum (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <bool HAS_WEIGHT, int FMT>
+__global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
+  extern __shared__ uint4 lds[];
+  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint32_t w = wave_index(p.hdr);
+  if (w >= p.q_waves) {
+    kvi_body<FMT>(p.k, w - p.q_waves, lds_wave);
+    // The compiler lays the two paths out one after the other; with the kv
+    // stores drained here, the q path's loads keep their per-load waits.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  } else {
+    qnr_body<HAS_WEIGHT>(p.q, w, lds_wave);
   }
 }
 
@@ -901,11 +951,17 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
   return launch(fn, p.units, kIrqChunkLog2, &p, (hipStream_t)stream);
 }
 
-int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
-               const uint16_t* norm_weight, const int64_t* positions,
-               const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
-               int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
-               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and parameter set-up shared by the standalone and the fused
+// entry points.  RQ_OK with `empty` set means there is nothing to launch.
+int prep_qnr(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+             const uint16_t* norm_weight, const int64_t* positions, const float* cos_sin_cache,
+             int64_t max_pos, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+             double eps, uint16_t* q_out, QnrParams& p, bool& empty) {
+  empty = true;
   if (n_tokens < 0 || n_heads_q < 1 || max_pos < 1) return RQ_ERR_SHAPE;
   if (q_head_padded < n_heads_q) return RQ_ERR_SHAPE;  // [P1] section 1 check
   if ((int64_t)n_tokens * q_head_padded >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
@@ -917,23 +973,22 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
       !aligned(positions, 8) || !aligned(cos_sin_cache, 16) || !aligned(q_out, 16) ||
       (norm_weight && !aligned(norm_weight, 16)))
     return RQ_ERR_ALIGN;
-  QnrParams p;
   p.q = q_in; p.q_st = q_stride_token; p.q_sh = q_stride_head;
   p.weight = norm_weight; p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
   p.units = (uint32_t)(n_tokens * q_head_padded);
   p.div_hpad = make_magic((uint32_t)q_head_padded);
   p.hq = (uint32_t)n_heads_q; p.hpad = (uint32_t)q_head_padded;
   p.eps = (float)eps; p.q_out = q_out;
-  const void* fn = norm_weight ? (const void*)qnr_kernel<true> : (const void*)qnr_kernel<false>;
-  return launch(fn, p.units, kQnrChunkLog2, &p, (hipStream_t)stream);
+  empty = false;
+  return RQ_OK;
 }
 
-int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
-                         const float* cos_sin_cache, int64_t max_pos,
-                         const int64_t* slot_mapping, int64_t n_tokens, uint8_t* k_cache,
-                         int64_t num_blocks, int64_t block_stride_bytes,
-                         int32_t cache_block_size, int32_t scale_fmt, double eps,
-                         void* stream) {
+int prep_kvi(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
+             const float* cos_sin_cache, int64_t max_pos, const int64_t* slot_mapping,
+             int64_t n_tokens, uint8_t* k_cache, int64_t num_blocks, int64_t block_stride_bytes,
+             int32_t cache_block_size, int32_t scale_fmt, double eps, KviParams& p,
+             bool& empty) {
+  empty = true;
   if (n_tokens < 0 || max_pos < 1 || num_blocks < 1 || cache_block_size < 1) return RQ_ERR_SHAPE;
   if (n_tokens >= (int64_t(1) << 27)) return RQ_ERR_SHAPE;
   if (num_blocks * (int64_t)cache_block_size >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
@@ -947,15 +1002,79 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
       !aligned(cos_sin_cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
       (block_stride_bytes % 16))
     return RQ_ERR_ALIGN;
-  KviParams p;
   p.kv = kv; p.kv_st = kv_stride_token; p.positions = positions; p.cs = cos_sin_cache;
   p.max_pos = max_pos; p.slots = slot_mapping; p.n_tokens = (uint32_t)n_tokens;
   p.num_slots = num_blocks * (int64_t)cache_block_size;
   p.div_bs = make_magic((uint32_t)cache_block_size); p.bs = (uint32_t)cache_block_size;
   p.cache = k_cache; p.block_stride = block_stride_bytes; p.eps = (float)eps;
+  empty = false;
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+               const uint16_t* norm_weight, const int64_t* positions,
+               const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+               int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
+               void* stream) {
+  QnrParams p;
+  bool empty;
+  const int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions,
+                          cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps, q_out,
+                          p, empty);
+  if (rc != RQ_OK || empty) return rc;
+  const void* fn = norm_weight ? (const void*)qnr_kernel<true> : (const void*)qnr_kernel<false>;
+  return launch(fn, p.units, kQnrChunkLog2, &p, (hipStream_t)stream);
+}
+
+int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
+                         const float* cos_sin_cache, int64_t max_pos,
+                         const int64_t* slot_mapping, int64_t n_tokens, uint8_t* k_cache,
+                         int64_t num_blocks, int64_t block_stride_bytes,
+                         int32_t cache_block_size, int32_t scale_fmt, double eps,
+                         void* stream) {
+  KviParams p;
+  bool empty;
+  const int rc = prep_kvi(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping,
+                          n_tokens, k_cache, num_blocks, block_stride_bytes, cache_block_size,
+                          scale_fmt, eps, p, empty);
+  if (rc != RQ_OK || empty) return rc;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)kvi_kernel<RQ_SCALE_FP32>;
   return launch(fn, p.n_tokens, kKviChunkLog2, &p, (hipStream_t)stream);
+}
+
+int qnorm_rope_kv_rope_quant_insert(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, uint16_t* q_out, uint8_t* k_cache, int64_t num_blocks,
+    int64_t block_stride_bytes, int32_t cache_block_size, int32_t scale_fmt, double quant_eps,
+    void* stream) {
+  FusedParams p;
+  bool eq, ek;
+  int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions, cos_sin_cache,
+                    max_pos, n_tokens, n_heads_q, q_head_padded, eps, q_out, p.q, eq);
+  if (rc != RQ_OK) return rc;
+  rc = prep_kvi(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping, n_tokens,
+                k_cache, num_blocks, block_stride_bytes, cache_block_size, scale_fmt, quant_eps,
+                p.k, ek);
+  if (rc != RQ_OK || eq) return rc;  // both are empty exactly when n_tokens == 0
+  p.q_waves = (p.q.units + 3u) / 4u;
+  const uint32_t kv_waves = (p.k.n_tokens + 3u) / 4u;
+  const void* fn;
+  if (norm_weight)
+    fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)fused_qnr_kvi_kernel<true, RQ_SCALE_UE8M0>
+                                     : (const void*)fused_qnr_kvi_kernel<true, RQ_SCALE_FP32>;
+  else
+    fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)fused_qnr_kvi_kernel<false, RQ_SCALE_UE8M0>
+                                     : (const void*)fused_qnr_kvi_kernel<false, RQ_SCALE_FP32>;
+  // `launch` sizes grids in 16-lane rows: 4 per wave
+  return launch(fn, 4u * (p.q_waves + kv_waves), kQnrChunkLog2, &p, (hipStream_t)stream);
 }
 
 int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,

@@ -154,6 +154,33 @@ def test_kvi_validation(kw, status):
     assert kvi(**kw) == status
 
 
+def fused(**kw):
+    a = dict(q=A, qst=64 * 512, qsh=512, w=A, kv=A, kst=512, pos=A, cs=A, max_pos=8192,
+             slots=A, n=8, hq=64, hpad=128, eps=1e-6, out=A, cache=A, nb=256, stride=64 * 528,
+             bs=64, fmt=0, qeps=1e-10)
+    a.update(kw)
+    return _lib.lib().qnorm_rope_kv_rope_quant_insert(
+        a["q"], a["qst"], a["qsh"], a["w"], a["kv"], a["kst"], a["pos"], a["cs"], a["max_pos"],
+        a["slots"], a["n"], a["hq"], a["hpad"], a["eps"], a["out"], a["cache"], a["nb"],
+        a["stride"], a["bs"], a["fmt"], a["qeps"], None)
+
+
+def test_fused_zero_tokens_is_ok_without_pointers():
+    assert fused(n=0, q=None, w=None, kv=None, pos=None, cs=None, slots=None, out=None,
+                 cache=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpad=63), SHAPE), (dict(bs=0), SHAPE), (dict(eps=0.0), VALUE), (dict(qeps=0.0), VALUE),
+    (dict(fmt=3), VALUE), (dict(q=None), NULL), (dict(kv=None), NULL), (dict(slots=None), NULL),
+    (dict(cache=None), NULL), (dict(stride=100), STRIDE), (dict(kv=A + 8), ALIGN),
+    (dict(out=A + 8), ALIGN),
+])
+def test_fused_validation(kw, status):
+    assert fused(**kw) == status
+
+
 def idx(**kw):
     a = dict(q=A, qst=64 * 128, qsh=128, pos=A, cs=A, max_pos=4096, w=A, wst=64, n=8, h=64,
              ss=128 ** -0.5, hs=1.0, eps=1e-10, out=A, ost=64 * 128, osh=128, wo=A, wost=64)
