@@ -56,6 +56,13 @@ def lib():
         L.orc_kv_rope_quant_insert.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, I32,
                                                I32, D]
         L.orc_kv_rope_quant_insert.restype = ctypes.c_int
+        L.orc_inv_rope_bf16.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, P, I64, I64]
+        L.orc_inv_rope_bf16.restype = ctypes.c_int
+        L.orc_qnorm_rope_fp8.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, I32, D,
+                                         P, P]
+        L.orc_qnorm_rope_fp8.restype = ctypes.c_int
+        L.orc_kv_rope_insert_full.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64]
+        L.orc_kv_rope_insert_full.restype = ctypes.c_int
         F = ctypes.c_float
         L.orc_indexer_rope.argtypes = [P, P, P]
         L.orc_indexer_rope.restype = None
@@ -208,6 +215,31 @@ def inv_rope_fp8_quant(o_bits, positions, cos_sin_cache, heads_per_group,
     return out, sc
 
 
+def inv_rope_bf16(o_bits, positions, cos_sin_cache, heads_per_group, layout="group"):
+    """Oracle inverse RoPE with bf16 output (the IRQ kernel without quantization).
+
+    layout "group": out uint16 [G, N, hpg*512]; layout "token": out [N, H, 512].
+    """
+    o_bits = _need(o_bits, np.uint16, "o")
+    positions = _need(positions, np.int64, "positions")
+    cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
+    N, H, D = o_bits.shape
+    assert D == 512
+    hpg = int(heads_per_group)
+    G = H // hpg
+    if layout == "group":
+        out = np.full((G, N, hpg * 512), 0xFFFF, dtype=np.uint16)
+        osg, ost = N * hpg * 512, hpg * 512
+    else:
+        out = np.full((N, H, 512), 0xFFFF, dtype=np.uint16)
+        osg, ost = hpg * 512, H * 512
+    rc = lib().orc_inv_rope_bf16(_ptr(o_bits), H * 512, 512, _ptr(positions),
+                                 _ptr(cos_sin_cache), cos_sin_cache.shape[0], N, H, hpg,
+                                 _ptr(out), osg, ost)
+    _check(rc, "inv_rope_bf16")
+    return out
+
+
 def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps):
     """Oracle QNR: q_bits uint16 [N, Hq, 512] -> q_out uint16 [N, Hpad, 512]."""
     q_bits = _need(q_bits, np.uint16, "q_in")
@@ -223,6 +255,48 @@ def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps
                               q_head_padded, eps, _ptr(q_out))
     _check(rc, "qnorm_rope")
     return q_out
+
+
+def qnorm_rope_fp8(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps,
+                   scale_fmt=SCALE_FP32, quant_eps=1e-10):
+    """Oracle q path into FP8: q_bits uint16 [N, Hq, 512] -> (codes uint8
+    [N, Hpad, 512], scales f32 [N, Hpad, 4] or, UE8M0, uint32 [N, Hpad])."""
+    q_bits = _need(q_bits, np.uint16, "q_in")
+    positions = _need(positions, np.int64, "positions")
+    cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
+    if weight_bits is not None:
+        weight_bits = _need(weight_bits, np.uint16, "weight")
+    N, Hq, D = q_bits.shape
+    assert D == 512
+    codes = np.full((N, q_head_padded, 512), 0xCD, dtype=np.uint8)
+    if scale_fmt == SCALE_UE8M0:
+        sc = np.full((N, q_head_padded), 0xDEADBEEF, dtype=np.uint32)
+    else:
+        sc = np.full((N, q_head_padded, 4), -1.0, dtype=np.float32)
+    rc = lib().orc_qnorm_rope_fp8(_ptr(q_bits), Hq * 512, 512, _ptr(weight_bits),
+                                  _ptr(positions), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                  N, Hq, q_head_padded, eps, scale_fmt, quant_eps, _ptr(codes),
+                                  _ptr(sc))
+    _check(rc, "qnorm_rope_fp8")
+    return codes, sc
+
+
+def kv_rope_insert_full(kv_bits, positions, cos_sin_cache, slot_mapping, cache):
+    """Oracle kv path into a token-strided bf16 cache: writes rows of ``cache``
+    (uint16 [num_slots, row_elems], row_elems >= 512) in place and returns it."""
+    kv_bits = _need(kv_bits, np.uint16, "kv")
+    positions = _need(positions, np.int64, "positions")
+    cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
+    slot_mapping = _need(slot_mapping, np.int64, "slot_mapping")
+    cache = _need(cache, np.uint16, "cache")
+    N, D = kv_bits.shape
+    assert D == 512
+    ns, row = cache.shape
+    rc = lib().orc_kv_rope_insert_full(_ptr(kv_bits), 512, _ptr(positions),
+                                       _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                       _ptr(slot_mapping), N, _ptr(cache), ns, row)
+    _check(rc, "kv_rope_insert_full")
+    return cache
 
 
 def kv_rope_quant_insert(kv_bits, positions, cos_sin_cache, slot_mapping, k_cache,

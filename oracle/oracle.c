@@ -10,7 +10,8 @@
  * Sources (web pages; cited by title and section, never by line):
  *   [P1] "vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선"
  *        (analysis of vLLM PR #49236) - sections 1 (the _out op and its
- *        argument checks) and 2 (the op schema).
+ *        argument checks) and 2 (the op schema, and the full-cache variants
+ *        named beside it).
  *   [P3] "vLLM, DeepSeek V4 모델의 저지연을 위한 RMSNorm과 라우터 GEMV 연산
  *        융합으로 성능 극대화" (analysis of vLLM PR #41263) - section 5 (the
  *        RMSNorm formula).
@@ -18,7 +19,8 @@
  *        FP8 quant 커널 3.5배 가속기" (analysis of vLLM PR #63540) - intro,
  *        section 1 (BLOCK_H and group addressing), section 2 (the register
  *        partner swap and the rotation formulas), section 3 (block amax,
- *        UE8M0 packing).
+ *        UE8M0 packing), section 4 (the kernel's compile keys, `quantize`
+ *        among them).
  *   [P5] "vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput
  *        향상" (analysis of vLLM PR #46862) - section 1 (power-of-two scale).
  *
@@ -309,6 +311,41 @@ int orc_inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_
   return ORC_OK;
 }
 
+/* ----------------------------------------------------- inv_rope_bf16 */
+
+/* The inverse RoPE alone, bf16 out: the IRQ kernel with its quantization
+ * switched off ([P4] section 4 lists `quantize` as a compile-time key of the
+ * kernel).  Reading: the same fp32 rotation as above, then one bf16 RNE
+ * rounding per element (so the 448 pass-through dims come out as bit copies),
+ * stored with the group addressing of the codes above, in elements:
+ *   out[g*out_stride_group + t*out_stride_token + j*512 + d]. */
+int orc_inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
+                      const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                      int64_t n_tokens, int32_t n_heads, int32_t heads_per_group,
+                      uint16_t* out, int64_t out_stride_group, int64_t out_stride_token) {
+  int64_t t;
+  int32_t h;
+  float x[HEAD_DIM], y[HEAD_DIM];
+  if (n_tokens < 0 || n_heads <= 0 || heads_per_group <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
+  if (n_heads % heads_per_group) return ORC_ERR_SHAPE;
+  if (n_tokens == 0) return ORC_OK;
+  if (!o || !positions || !cos_sin_cache || !out) return ORC_ERR_NULL;
+  for (t = 0; t < n_tokens; ++t)
+    if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ERR_VALUE;
+  for (t = 0; t < n_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * ROPE_DIM;
+    for (h = 0; h < n_heads; ++h) {
+      int64_t g = h / heads_per_group, j = h % heads_per_group;
+      uint16_t* dst = out + g * out_stride_group + t * out_stride_token + j * HEAD_DIM;
+      int d;
+      load_head(o + t * o_stride_token + (int64_t)h * o_stride_head, x);
+      orc_rope_head(x, y, row, 1);
+      for (d = 0; d < HEAD_DIM; ++d) dst[d] = orc_f32_to_bf16(y[d]);
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---------------------------------------------------------- qnorm_rope */
 
 /* q_in[N, Hq, 512] bf16 -> per-head RMSNorm -> forward RoPE -> bf16 RNE into
@@ -344,6 +381,58 @@ int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
       orc_rmsnorm_head(x, norm_weight, epsf, y);
       orc_rope_head(y, z, row, 0);
       for (d = 0; d < HEAD_DIM; ++d) dst[d] = orc_f32_to_bf16(z[d]);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------ qnorm_rope_fp8 */
+
+/* The q path into a separate FP8 tensor, one of the full-cache variants named
+ * beside the op schema in [P1] section 2.  Readings (the pages give only the
+ * variant's name): RMSNorm and forward RoPE exactly as in orc_qnorm_rope, in
+ * fp32; the fp32 head (not its bf16 rounding: the same fusion as the kv path)
+ * goes through orc_quant_head; a pad head h in [Hq, Hpad) is a zero head
+ * quantized the same way (codes +0, scales from eps).  Layout:
+ *   codes   q_fp8[(t*Hpad + h)*512 + d]                          (bytes)
+ *   FP32    q_scales[(t*Hpad + h)*4 + b]                         (floats)
+ *   UE8M0   q_scales[t*Hpad + h]                          (uint32 words) */
+int orc_qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+                       const uint16_t* norm_weight, const int64_t* positions,
+                       const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+                       int32_t n_heads_q, int32_t q_head_padded, double eps, int32_t scale_fmt,
+                       double quant_eps, uint8_t* q_fp8, void* q_scales) {
+  int64_t t;
+  int32_t h;
+  int b;
+  float x[HEAD_DIM], y[HEAD_DIM], z[HEAD_DIM], sf[NBLOCK];
+  uint32_t word;
+  float epsf = (float)eps, qepsf = (float)quant_eps;
+  if (n_tokens < 0 || n_heads_q <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
+  if (q_head_padded < n_heads_q) return ORC_ERR_SHAPE;
+  if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
+  if (scale_fmt != ORC_SCALE_FP32 && scale_fmt != ORC_SCALE_UE8M0) return ORC_ERR_VALUE;
+  if (!eps_ok(quant_eps)) return ORC_ERR_VALUE;
+  if (n_tokens == 0) return ORC_OK;
+  if (!q_in || !positions || !cos_sin_cache || !q_fp8 || !q_scales) return ORC_ERR_NULL;
+  for (t = 0; t < n_tokens; ++t)
+    if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ERR_VALUE;
+  for (t = 0; t < n_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * ROPE_DIM;
+    for (h = 0; h < q_head_padded; ++h) {
+      int64_t u = t * q_head_padded + h;
+      if (h < n_heads_q) {
+        load_head(q_in + t * q_stride_token + (int64_t)h * q_stride_head, x);
+        orc_rmsnorm_head(x, norm_weight, epsf, y);
+        orc_rope_head(y, z, row, 0);
+      } else {
+        memset(z, 0, sizeof z);
+      }
+      orc_quant_head(z, scale_fmt, qepsf, q_fp8 + u * HEAD_DIM, sf, &word);
+      if (scale_fmt == ORC_SCALE_UE8M0)
+        ((uint32_t*)q_scales)[u] = word;
+      else
+        for (b = 0; b < NBLOCK; ++b) ((float*)q_scales)[u * NBLOCK + b] = sf[b];
     }
   }
   return ORC_OK;
@@ -401,6 +490,44 @@ int orc_kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
     } else {
       for (b = 0; b < NBLOCK; ++b) memcpy(rec + HEAD_DIM + 4 * b, &sf[b], 4);
     }
+  }
+  return ORC_OK;
+}
+
+/* --------------------------------------------------- kv_rope_insert_full */
+
+/* The kv path into a contiguous, token-strided cache, the other full-cache
+ * variant named beside the op schema in [P1] section 2.  Readings (the pages
+ * give only "512 wide" and "token strided"): the cache holds bf16 rows of 512
+ * (no quantization, hence no scales), slot s owns the row at
+ * cache + s*cache_stride_token (elements); forward RoPE as in
+ * orc_kv_rope_quant_insert, then one bf16 RNE rounding.  s < 0 skips the
+ * token; s >= num_slots and repeated slots are rejected; nothing else is
+ * written. */
+int orc_kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token,
+                            const int64_t* positions, const float* cos_sin_cache,
+                            int64_t max_pos, const int64_t* slot_mapping, int64_t n_tokens,
+                            uint16_t* cache, int64_t num_slots, int64_t cache_stride_token) {
+  int64_t t, u;
+  int d;
+  float x[HEAD_DIM], y[HEAD_DIM];
+  if (n_tokens < 0 || max_pos <= 0 || num_slots <= 0) return ORC_ERR_SHAPE;
+  if (cache_stride_token < HEAD_DIM) return ORC_ERR_STRIDE;
+  if (n_tokens == 0) return ORC_OK;
+  if (!kv || !positions || !cos_sin_cache || !slot_mapping || !cache) return ORC_ERR_NULL;
+  for (t = 0; t < n_tokens; ++t) {
+    if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ERR_VALUE;
+    if (slot_mapping[t] >= num_slots) return ORC_ERR_VALUE;
+    if (slot_mapping[t] >= 0)
+      for (u = 0; u < t; ++u)
+        if (slot_mapping[u] == slot_mapping[t]) return ORC_ERR_VALUE;
+  }
+  for (t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    load_head(kv + t * kv_stride_token, x);
+    orc_rope_head(x, y, cos_sin_cache + positions[t] * ROPE_DIM, 0);
+    for (d = 0; d < HEAD_DIM; ++d) cache[s * cache_stride_token + d] = orc_f32_to_bf16(y[d]);
   }
   return ORC_OK;
 }
