@@ -7,7 +7,9 @@
  *        (analysis of vLLM PR #49236): section 1 defines the fused q-norm/RoPE
  *        and kv-RoPE/quant/insert op with a caller-allocated q_out and lists its
  *        argument checks; section 2 gives its schema (outputs mutated, returns
- *        nothing).
+ *        nothing), and names beside it the full-cache forms: q written in
+ *        place (bf16) or to a separate FP8 tensor, kv into a contiguous,
+ *        512-wide, token-strided cache.
  *   [P3] "vLLM, DeepSeek V4 모델의 저지연을 위한 RMSNorm과 라우터 GEMV 연산
  *        융합으로 성능 극대화" (analysis of vLLM PR #41263): section 5 gives the
  *        RMSNorm formula.
@@ -15,7 +17,8 @@
  *        FP8 quant 커널 3.5배 가속기" (analysis of vLLM PR #63540): intro (the
  *        op sits before the wo_a projection), section 1 (heads grouped per
  *        wo_a group, scale column = head_in_group * 4 + block), section 2 (the
- *        GPT-J inverse rotation), section 3 (block-128 amax, UE8M0 packing).
+ *        GPT-J inverse rotation), section 3 (block-128 amax, UE8M0 packing),
+ *        section 4 (the kernel's compile keys, among them `quantize`).
  *   [P5] "vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput
  *        향상" (analysis of vLLM PR #46862): section 1 (the fused indexer
  *        query kernel: rotate-half RoPE with a bf16 round trip, power-of-two
@@ -59,7 +62,7 @@
 extern "C" {
 #endif
 
-#define ROPEQUANT_ABI_VERSION 1
+#define ROPEQUANT_ABI_VERSION 2
 
 enum {
   RQ_OK = 0,
@@ -94,7 +97,10 @@ enum {
  * Default (group-major, what wo_a consumes) layout: out [G, N, hpg*512] with
  * strides (N*hpg*512, hpg*512); FP32 scales [G, N, hpg*4] with strides
  * (N*hpg*4, hpg*4, 1); UE8M0 scales [G, N, hpg] with strides (N*hpg, hpg, 1).
- * Token-major [N, H, 512] is out strides (hpg*512, H*512).
+ * Token-major [N, H, 512] is out strides (hpg*512, H*512).  Scales may also be
+ * laid out MN-major for a GEMM that reads them per column (token fastest):
+ * FP32 [G, hpg*4, N] is strides (hpg*4*N, 1, N); UE8M0 [G, hpg, N] is
+ * (hpg*N, 1, N).
  *
  * o: bf16 [N, H, 512] with strides (o_stride_token, o_stride_head, 1); base
  *    16-byte aligned, strides positive multiples of 8.
@@ -110,6 +116,25 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
                        uint8_t* out, int64_t out_stride_group, int64_t out_stride_token,
                        void* scales, int64_t sc_stride_group, int64_t sc_stride_token,
                        int64_t sc_stride_block, void* stream);
+
+/*
+ * inv_rope_bf16 - the inverse RoPE of inv_rope_fp8_quant with the
+ * quantization switched off ([P4] section 4 lists `quantize` among the
+ * kernel's compile keys), for a wo_a projection that takes bf16:
+ *   out[g*out_stride_group + t*out_stride_token + j*512 + d] = bf16_rne(x'_d)
+ * with x', g, j as above (pass-through dims are thus copied bit for bit).
+ * out: bf16, 16-byte aligned, strides (elements) positive multiples of 8,
+ *   rows must not overlap.  Group-major [G, N, hpg*512] is strides
+ *   (N*hpg*512, hpg*512); token-major [N, H, 512] is (hpg*512, H*512).
+ *   out may be o itself only in that token-major form with o laid out
+ *   [N, H, 512] (o_stride_head 512): each head then overwrites its own row;
+ *   other aliasing returns RQ_ERR_STRIDE when out == o and is undefined
+ *   otherwise.  A head whose position is out of range is written as bf16 NaN.
+ */
+int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
+                  const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                  int64_t n_tokens, int32_t n_heads, int32_t heads_per_group, uint16_t* out,
+                  int64_t out_stride_group, int64_t out_stride_token, void* stream);
 
 /*
  * qnorm_rope - per-head RMSNorm and forward RoPE of the queries, written into
@@ -130,13 +155,36 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
  *   16-byte aligned, strides positive multiples of 8.  norm_weight: bf16
  *   [512] or NULL, 16-byte aligned.  q_out: bf16 [N, q_head_padded, 512]
  *   contiguous, 16-byte aligned.  eps: RMSNorm epsilon (> 0, fp32-finite).
- *   n_tokens * q_head_padded < 2^31.
+ *   n_tokens * q_head_padded < 2^31.  In place ([P1] section 2's full-cache
+ *   form): q_out may be q_in itself when q_head_padded == n_heads_q and q_in
+ *   is contiguous; q_out == q_in with any other shape returns RQ_ERR_STRIDE.
  */
 int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
                const uint16_t* norm_weight, const int64_t* positions,
                const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
                int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
                void* stream);
+
+/*
+ * qnorm_rope_fp8 - the q path written to a separate FP8 tensor ([P1] section
+ * 2's full-cache form).  y' as in qnorm_rope, kept in fp32 (not rounded to
+ * bf16), then block-128 quantized as in inv_rope_fp8_quant with quant_eps as
+ * the amax floor; a pad head (n_heads_q <= h < q_head_padded) is a zero head
+ * quantized the same way: codes +0, scales quant_eps / 448 (FP32) or the
+ * power of two covering it (UE8M0).  With u = t * q_head_padded + h:
+ *   q_fp8[u*512 + d]                                   (e4m3 [N, Hpad, 512])
+ *   RQ_SCALE_FP32 : ((float*)q_scales)[u*4 + b] = s_b  (fp32 [N, Hpad, 4])
+ *   RQ_SCALE_UE8M0: ((uint32_t*)q_scales)[u]           ([N, Hpad], packed as
+ *                   in inv_rope_fp8_quant)
+ * q_fp8 16-byte aligned; q_scales 4-byte aligned; quant_eps >= 2^-116 as
+ * fp32.  A live head whose position is out of range gets NaN scales.  Other
+ * arguments as in qnorm_rope.
+ */
+int qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+                   const uint16_t* norm_weight, const int64_t* positions,
+                   const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+                   int32_t n_heads_q, int32_t q_head_padded, double eps, int32_t scale_fmt,
+                   double quant_eps, uint8_t* q_fp8, void* q_scales, void* stream);
 
 /*
  * kv_rope_quant_insert - forward RoPE and block-128 FP8 quantization of the
@@ -166,6 +214,23 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token,
                          void* stream);
 
 /*
+ * kv_rope_insert_full - forward RoPE of kv into a contiguous token-strided
+ * bf16 cache ([P1] section 2's full-cache form): for t < n_tokens with
+ * s = slot_mapping[t] >= 0,
+ *   cache[s * cache_stride_token + d] = bf16_rne(x'_d),  d < 512
+ * x' as in kv_rope_quant_insert.  s < 0 skips the token; s >= num_slots is
+ * skipped too (caller contract: slots unique and below num_slots).  No other
+ * element is written; a token whose position is out of range gets a NaN row.
+ * cache: bf16 [num_slots, cache_stride_token], 16-byte aligned;
+ *   cache_stride_token >= 512 and a multiple of 8.  kv as in
+ *   kv_rope_quant_insert.
+ */
+int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token,
+                        const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                        const int64_t* slot_mapping, int64_t n_tokens, uint16_t* cache,
+                        int64_t num_slots, int64_t cache_stride_token, void* stream);
+
+/*
  * qnorm_rope_kv_rope_quant_insert - qnorm_rope and kv_rope_quant_insert in a
  * single launch, the op's own shape in [P1] section 1 (the `_out` form: q_out
  * and k_cache preallocated by the caller, nothing returned; section 2 gives
@@ -182,6 +247,29 @@ int qnorm_rope_kv_rope_quant_insert(
     double eps, uint16_t* q_out, uint8_t* k_cache, int64_t num_blocks,
     int64_t block_stride_bytes, int32_t cache_block_size, int32_t scale_fmt, double quant_eps,
     void* stream);
+
+/*
+ * qnorm_rope_kv_rope_insert_full and qnorm_rope_fp8_kv_rope_insert_full - the
+ * full-cache forms of the fused op ([P1] section 2) in one launch: the q path
+ * of qnorm_rope (q_out, in place allowed as there) or of qnorm_rope_fp8, and
+ * the kv path of kv_rope_insert_full.  Bit-identical to the two separate
+ * calls; validation is the union of both.
+ */
+int qnorm_rope_kv_rope_insert_full(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, uint16_t* q_out, uint16_t* cache, int64_t num_slots, int64_t cache_stride_token,
+    void* stream);
+
+int qnorm_rope_fp8_kv_rope_insert_full(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, int32_t scale_fmt, double quant_eps, uint8_t* q_fp8, void* q_scales,
+    uint16_t* cache, int64_t num_slots, int64_t cache_stride_token, void* stream);
 
 /*
  * indexer_q_rope_quant - the sparse-attention indexer's query path ([P5]

@@ -10,9 +10,11 @@ helpers allocate correctly shaped outputs.
 
 Sources: the op semantics follow the analyses of vLLM PR #63540
 ("한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE + FP8 quant
-커널 3.5배 가속기", sections 1-3) for ``inv_rope_fp8_quant`` and of vLLM PR
+커널 3.5배 가속기", sections 1-4) for ``inv_rope_fp8_quant`` and ``inv_rope_bf16``
+and of vLLM PR
 #49236 ("vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선",
-sections 1-2) for ``qnorm_rope`` and ``kv_rope_quant_insert``, and of vLLM PR
+sections 1-2) for ``qnorm_rope`` and ``kv_rope_quant_insert`` and their
+full-cache forms (section 2), and of vLLM PR
 #46862 ("vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput 향상",
 section 1) for ``indexer_q_rope_quant``.
 """
@@ -21,10 +23,12 @@ import torch
 from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, lib
 
 __all__ = [
-    "inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
-    "qnorm_rope_kv_rope_quant_insert", "indexer_q_rope_quant",
-    "empty_inv_rope_fp8_quant_outputs", "empty_kv_cache", "set_block_threads",
-    "abi_version", "RopeQuantError", "RECORD_BYTES", "SCALE_FMTS",
+    "inv_rope_fp8_quant", "inv_rope_bf16", "qnorm_rope", "qnorm_rope_fp8",
+    "kv_rope_quant_insert", "kv_rope_insert_full", "qnorm_rope_kv_rope_quant_insert",
+    "qnorm_rope_kv_rope_insert_full", "qnorm_rope_fp8_kv_rope_insert_full",
+    "indexer_q_rope_quant", "empty_inv_rope_fp8_quant_outputs", "empty_qnorm_rope_fp8_outputs",
+    "empty_kv_cache", "set_block_threads", "abi_version", "RopeQuantError", "RECORD_BYTES",
+    "SCALE_FMTS",
 ]
 
 RECORD_BYTES = 528
@@ -87,6 +91,17 @@ def empty_inv_rope_fp8_quant_outputs(n_tokens, n_heads, heads_per_group, device,
     return out, sc
 
 
+def empty_qnorm_rope_fp8_outputs(n_tokens, q_head_padded, device, scale_fmt="fp32"):
+    """Codes uint8 [N, Hpad, 512] and scales float32 [N, Hpad, 4] (fp32) or
+    int32 [N, Hpad] (ue8m0 words)."""
+    codes = torch.empty((n_tokens, q_head_padded, 512), dtype=torch.uint8, device=device)
+    if _fmt(scale_fmt) == RQ_SCALE_UE8M0:
+        sc = torch.empty((n_tokens, q_head_padded), dtype=torch.int32, device=device)
+    else:
+        sc = torch.empty((n_tokens, q_head_padded, 4), dtype=torch.float32, device=device)
+    return codes, sc
+
+
 def empty_kv_cache(num_blocks, cache_block_size, device, fill=None):
     """uint8 [num_blocks, cache_block_size * 528] paged cache."""
     if fill is None:
@@ -106,14 +121,7 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
     "fp32" or int32/uint32 [G, N, hpg] words for "ue8m0" (any strides).
     """
     fmt = _fmt(scale_fmt)
-    _cuda(o, "o")
-    if o.dtype != torch.bfloat16 or o.dim() != 3 or o.shape[2] != 512 or o.stride(2) != 1:
-        raise ValueError("o must be bf16 [N, H, 512] with a contiguous last dim")
-    N, H, _ = o.shape
-    hpg = int(heads_per_group)
-    if hpg < 1 or H % hpg:
-        raise ValueError("heads_per_group must divide the head count")
-    G = H // hpg
+    N, H, hpg, G = _check_o(o, heads_per_group)
     _check_rope_inputs(positions, cos_sin_cache, N)
     if out.dtype not in _BYTE_DTYPES or tuple(out.shape) != (G, N, hpg * 512) or (
             out.stride(2) != 1):
@@ -135,24 +143,78 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
     check("inv_rope_fp8_quant", rc)
 
 
-def _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out):
+def _check_o(o, heads_per_group):
+    _cuda(o, "o")
+    if o.dtype != torch.bfloat16 or o.dim() != 3 or o.shape[2] != 512 or o.stride(2) != 1:
+        raise ValueError("o must be bf16 [N, H, 512] with a contiguous last dim")
+    N, H, _ = o.shape
+    hpg = int(heads_per_group)
+    if hpg < 1 or H % hpg:
+        raise ValueError("heads_per_group must divide the head count")
+    return N, H, hpg, H // hpg
+
+
+def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None):
+    """Inverse RoPE alone (the quantize-off form of inv_rope_fp8_quant): o
+    [N, H, 512] bf16 into out bf16 [G, N, hpg*512] (any strides on the first
+    two dims, last dim contiguous; the token-major view
+    ``t.view(N, G, hpg*512).transpose(0, 1)`` of a [N, H, 512] tensor works,
+    and that view of o itself rotates o in place)."""
+    N, H, hpg, G = _check_o(o, heads_per_group)
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (G, N, hpg * 512) or (
+            out.stride(2) != 1):
+        raise ValueError(f"out must be bf16 [{G}, {N}, {hpg * 512}], last dim contiguous")
+    _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"))
+    rc = lib().inv_rope_bf16(
+        o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0], N, H, hpg, out.data_ptr(), out.stride(0), out.stride(1),
+        _stream(o.device, stream))
+    check("inv_rope_bf16", rc)
+
+
+def _check_q_in(q_in, norm_weight, positions, cos_sin_cache):
     _cuda(q_in, "q_in")
     if q_in.dtype != torch.bfloat16 or q_in.dim() != 3 or q_in.shape[2] != 512 or (
             q_in.stride(2) != 1):
         raise ValueError("q_in must be bf16 [N, Hq, 512] with a contiguous last dim")
     N, Hq, _ = q_in.shape
     _check_rope_inputs(positions, cos_sin_cache, N)
-    if (q_out.dtype != q_in.dtype or q_out.dim() != 3 or q_out.shape[0] != N
-            or q_out.shape[2] != 512 or not q_out.is_contiguous()):
-        raise ValueError("q_out must be contiguous bf16 [N, q_head_padded, 512]")
-    if q_out.shape[1] < Hq:
-        raise ValueError("q_head_padded must be >= num_heads_q")
     if norm_weight is not None and (norm_weight.dtype != torch.bfloat16
                                     or tuple(norm_weight.shape) != (512,)
                                     or not norm_weight.is_contiguous()):
         raise ValueError("norm_weight must be contiguous bf16 [512] or None")
     _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
-                 (q_out, "q_out"), (norm_weight, "norm_weight"))
+                 (norm_weight, "norm_weight"))
+    return N, Hq
+
+
+def _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq):
+    if (q_fp8.dtype not in _BYTE_DTYPES or q_fp8.dim() != 3 or q_fp8.shape[0] != N
+            or q_fp8.shape[2] != 512 or not q_fp8.is_contiguous()):
+        raise ValueError("q_fp8 must be contiguous uint8/float8_e4m3fn [N, q_head_padded, 512]")
+    hpad = q_fp8.shape[1]
+    if hpad < Hq:
+        raise ValueError("q_head_padded must be >= num_heads_q")
+    if fmt == RQ_SCALE_UE8M0:
+        if q_scales.dtype not in _WORD_DTYPES or tuple(q_scales.shape) != (N, hpad) or (
+                not q_scales.is_contiguous()):
+            raise ValueError(f"ue8m0 q_scales must be contiguous int32/uint32 [{N}, {hpad}]")
+    elif q_scales.dtype != torch.float32 or tuple(q_scales.shape) != (N, hpad, 4) or (
+            not q_scales.is_contiguous()):
+        raise ValueError(f"fp32 q_scales must be contiguous float32 [{N}, {hpad}, 4]")
+    _same_device(q_in, (q_fp8, "q_fp8"), (q_scales, "q_scales"))
+    return hpad
+
+
+def _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out):
+    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    if (q_out.dtype != q_in.dtype or q_out.dim() != 3 or q_out.shape[0] != N
+            or q_out.shape[2] != 512 or not q_out.is_contiguous()):
+        raise ValueError("q_out must be contiguous bf16 [N, q_head_padded, 512]")
+    if q_out.shape[1] < Hq:
+        raise ValueError("q_head_padded must be >= num_heads_q")
+    _same_device(q_in, (q_out, "q_out"))
     return N, Hq
 
 
@@ -174,6 +236,23 @@ def _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_
     return N
 
 
+def _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache):
+    _cuda(kv, "kv")
+    if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != 512 or kv.stride(1) != 1:
+        raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
+    N = kv.shape[0]
+    _check_rope_inputs(positions, cos_sin_cache, N)
+    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
+            or not slot_mapping.is_contiguous()):
+        raise ValueError("slot_mapping must be contiguous int64 [N]")
+    if (cache.dtype != torch.bfloat16 or cache.dim() != 2 or cache.shape[1] < 512
+            or cache.stride(1) != 1):
+        raise ValueError("cache must be bf16 [num_slots, >= 512] with a contiguous last dim")
+    _same_device(kv, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                 (slot_mapping, "slot_mapping"), (cache, "cache"))
+    return N
+
+
 def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, stream=None):
     """Per-head RMSNorm + forward RoPE of q_in [N, Hq, 512] bf16 into the
     contiguous q_out [N, q_head_padded, 512] bf16; pad heads are zeroed.
@@ -186,6 +265,34 @@ def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, str
         cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, q_out.shape[1], float(eps),
         q_out.data_ptr(), _stream(q_in.device, stream))
     check("qnorm_rope", rc)
+
+
+def qnorm_rope_fp8(q_in, norm_weight, positions, cos_sin_cache, q_fp8, q_scales, eps=1e-6,
+                   scale_fmt="fp32", quant_eps=1e-10, stream=None):
+    """qnorm_rope's q path written to FP8: block-128 e4m3 codes q_fp8
+    [N, q_head_padded, 512] and scales q_scales (float32 [N, Hpad, 4], or
+    int32/uint32 [N, Hpad] UE8M0 words); pad heads are quantized zero heads."""
+    fmt = _fmt(scale_fmt)
+    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
+    rc = lib().qnorm_rope_fp8(
+        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
+        None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
+        cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, hpad, float(eps), fmt,
+        float(quant_eps), q_fp8.data_ptr(), q_scales.data_ptr(), _stream(q_in.device, stream))
+    check("qnorm_rope_fp8", rc)
+
+
+def kv_rope_insert_full(kv, positions, cos_sin_cache, slot_mapping, cache, stream=None):
+    """Forward RoPE of kv [N, 512] bf16 into the token-strided bf16 cache
+    [num_slots, >= 512]: token t's row goes to cache[slot_mapping[t], :512]
+    (skipped for a negative slot)."""
+    N = _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache)
+    rc = lib().kv_rope_insert_full(
+        kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, cache.data_ptr(), cache.shape[0],
+        cache.stride(0), _stream(kv.device, stream))
+    check("kv_rope_insert_full", rc)
 
 
 def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size,
@@ -218,6 +325,42 @@ def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_ca
         k_cache.data_ptr(), k_cache.shape[0], k_cache.stride(0), int(cache_block_size), fmt,
         float(quant_eps), _stream(q_in.device, stream))
     check("qnorm_rope_kv_rope_quant_insert", rc)
+
+
+def qnorm_rope_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cache,
+                                   slot_mapping, q_out, cache, eps=1e-6, stream=None):
+    """Full-cache form of the fused op in one launch: qnorm_rope (q_out may be
+    q_in itself) and kv_rope_insert_full."""
+    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
+    if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
+        raise ValueError("q_in and kv must have the same number of tokens")
+    rc = lib().qnorm_rope_kv_rope_insert_full(
+        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
+        None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
+        positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+        slot_mapping.data_ptr(), N, Hq, q_out.shape[1], float(eps), q_out.data_ptr(),
+        cache.data_ptr(), cache.shape[0], cache.stride(0), _stream(q_in.device, stream))
+    check("qnorm_rope_kv_rope_insert_full", rc)
+
+
+def qnorm_rope_fp8_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cache,
+                                       slot_mapping, q_fp8, q_scales, cache, eps=1e-6,
+                                       scale_fmt="fp32", quant_eps=1e-10, stream=None):
+    """Full-cache form of the fused op with q to FP8, in one launch:
+    qnorm_rope_fp8 and kv_rope_insert_full."""
+    fmt = _fmt(scale_fmt)
+    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
+    if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
+        raise ValueError("q_in and kv must have the same number of tokens")
+    rc = lib().qnorm_rope_fp8_kv_rope_insert_full(
+        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
+        None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
+        positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+        slot_mapping.data_ptr(), N, Hq, hpad, float(eps), fmt, float(quant_eps),
+        q_fp8.data_ptr(), q_scales.data_ptr(), cache.data_ptr(), cache.shape[0], cache.stride(0),
+        _stream(q_in.device, stream))
+    check("qnorm_rope_fp8_kv_rope_insert_full", rc)
 
 
 def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_out,

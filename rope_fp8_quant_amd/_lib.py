@@ -14,9 +14,11 @@ RQ_OK = 0
 RQ_SCALE_FP32 = 0
 RQ_SCALE_UE8M0 = 1
 
-EXPORTS = ("inv_rope_fp8_quant", "qnorm_rope", "kv_rope_quant_insert",
-           "qnorm_rope_kv_rope_quant_insert", "indexer_q_rope_quant",
-           "ropequant_strerror", "ropequant_abi_version", "ropequant_set_block_threads")
+EXPORTS = ("inv_rope_fp8_quant", "inv_rope_bf16", "qnorm_rope", "qnorm_rope_fp8",
+           "kv_rope_quant_insert", "kv_rope_insert_full", "qnorm_rope_kv_rope_quant_insert",
+           "qnorm_rope_kv_rope_insert_full", "qnorm_rope_fp8_kv_rope_insert_full",
+           "indexer_q_rope_quant", "ropequant_strerror", "ropequant_abi_version",
+           "ropequant_set_block_threads")
 
 _lock = threading.Lock()
 _lib = None
@@ -47,8 +49,22 @@ def lib():
         L.inv_rope_fp8_quant.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, I32, D,
                                          P, I64, I64, P, I64, I64, I64, P]
         L.inv_rope_fp8_quant.restype = I
+        L.inv_rope_bf16.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, P, I64, I64, P]
+        L.inv_rope_bf16.restype = I
         L.qnorm_rope.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, P, P]
         L.qnorm_rope.restype = I
+        L.qnorm_rope_fp8.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, I32, D, P, P,
+                                     P]
+        L.qnorm_rope_fp8.restype = I
+        L.kv_rope_insert_full.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, P]
+        L.kv_rope_insert_full.restype = I
+        L.qnorm_rope_kv_rope_insert_full.argtypes = [P, I64, I64, P, P, I64, P, P, I64, P, I64,
+                                                     I32, I32, D, P, P, I64, I64, P]
+        L.qnorm_rope_kv_rope_insert_full.restype = I
+        L.qnorm_rope_fp8_kv_rope_insert_full.argtypes = [P, I64, I64, P, P, I64, P, P, I64, P,
+                                                         I64, I32, I32, D, I32, D, P, P, P, I64,
+                                                         I64, P]
+        L.qnorm_rope_fp8_kv_rope_insert_full.restype = I
         L.kv_rope_quant_insert.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, I32, I32, D,
                                            P]
         L.kv_rope_quant_insert.restype = I

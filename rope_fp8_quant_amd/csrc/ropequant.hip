@@ -272,6 +272,79 @@ __device__ __forceinline__ uint32_t pack_ue8m0(uint32_t ebyte, int q) {
   return w;
 }
 
+// Output forms of a kernel's 512-dim results: block FP8 with fp32 or UE8M0
+// scales (the RQ_SCALE_* values), or plain bf16 (no quantization).
+constexpr int kOutBf16 = 2;
+
+// The lane's 32 values rounded to bf16 (RNE), chunk m in outv[m]: the
+// layout the bf16 row store below takes.
+__device__ __forceinline__ void pack_bf16(const Vals& v, uint4 (&outv)[4]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 f = {v.x[k][2 * i], v.x[k][2 * i + 1]};
+      o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    outv[k] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  }
+}
+
+// Stores of the wave's four 512-dim results, staged back through LDS so
+// that every store instruction writes whole rows.  dst[k] is unit k's
+// destination; it is written only when ok[k] (wave-uniform) is set.
+//
+// bf16: lane L of row q holds, in outv[m], dims lane_dim0(L) + 32m of unit q.
+// Through LDS with the input side's slot swizzle, each store then writes one
+// unit's contiguous 1 KiB.
+__device__ __forceinline__ void store_rows_bf16(uint4* lds_wave, const uint4 (&outv)[4], int lane,
+                                                uint8_t* const (&dst)[4],
+                                                const bool (&ok)[4]) {
+  const int q = lane >> 4, L = lane & 15, b = L >> 2, r = L & 3;
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+#pragma unroll
+  for (int m = 0; m < 4; ++m) lds_wave[64 * q + 16 * b + r + 4 * (m ^ b)] = outv[m];
+  wave_lds_sync();
+  const int rslot = lane ^ (((lane >> 4) & 3) << 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (ok[k]) reinterpret_cast<uint4*>(dst[k])[lane] = lds_wave[64 * k + rslot];
+}
+
+// e4m3 codes (chunk m in codes[2m], codes[2m+1]): each store writes one
+// unit's 512 contiguous bytes.  8-byte granule G of unit q sits in LDS at
+// G ^ ((((G >> 4) & 3) ^ (q & 1)) << 2), which keeps both the per-lane writes
+// and the row reads free of bank conflicts.  Lanes 0..31 store units 0 and 2,
+// lanes 32..63 units 1 and 3 (constant indices throughout, so the base
+// pointers stay in scalar registers).  Unit k is stored when
+// unit0 + k < units (a tail wave past the last unit stores nothing).
+__device__ __forceinline__ void store_rows_fp8(uint4* lds_wave, const uint32_t (&codes)[8],
+                                               int lane, uint8_t* const (&dst)[4],
+                                               uint32_t unit0, uint32_t units) {
+  const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+  uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int G = 16 * blk + r + 4 * m;
+    lds8[64 * q + (G ^ (((blk ^ (q & 1)) & 3) << 2))] = make_uint2(codes[2 * m], codes[2 * m + 1]);
+  }
+  wave_lds_sync();
+  const int half = lane >> 5, j16 = lane & 31;
+  uint8_t* const base01 = half ? dst[1] : dst[0];
+  uint8_t* const base23 = half ? dst[3] : dst[2];
+  const int G0 = 2 * j16;
+  const int sw = (G0 >> 4) & 3;
+  const uint4 c01 = *reinterpret_cast<const uint4*>(lds8 + 64 * half + (G0 ^ ((sw ^ half) << 2)));
+  const uint4 c23 =
+      *reinterpret_cast<const uint4*>(lds8 + 64 * (2 + half) + (G0 ^ ((sw ^ half) << 2)));
+  if (unit0 + half < units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
+  if (unit0 + 2 + half < units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
+}
+
 // Launch shape, filled in by the host: every params struct starts with it.
 struct LaunchHdr {
   uint32_t wpb_log2;    // log2(waves per workgroup)
@@ -315,8 +388,11 @@ __device__ __forceinline__ T pick_row(int q, T v0, T v1, T v2, T v3) {
 }
 #define PICK_ROW(q, a) pick_row((q), (a)[0], (a)[1], (a)[2], (a)[3])
 
-template <int FMT>
+// OUT: RQ_SCALE_FP32 / RQ_SCALE_UE8M0 (codes and scales), or kOutBf16 (the
+// rotation only, bf16 rows in the same group-major places).
+template <int OUT>
 __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
+  constexpr bool kBf16 = OUT == kOutBf16;
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
@@ -331,6 +407,7 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   uint32_t badk[4];
   uint8_t* outk[4];
   uint8_t* sck[4];  // the unit's first scale
+  bool ok[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t u = min(unit0 + k, p.units - 1u);
@@ -340,10 +417,12 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     const uint32_t j = h - g * p.hpg;
     rows[k] = p.o + (int64_t)t * p.o_st + (int64_t)h * p.o_sh;
     posk[k] = load_uniform(p.positions + t);
-    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim;
+    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st +
+              (int64_t)j * (kBf16 ? 2 * kHeadDim : kHeadDim);
     const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                          (int64_t)(FMT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
+                          (int64_t)(OUT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
     sck[k] = static_cast<uint8_t*>(p.scales) + 4 * first;
+    ok[k] = unit0 + k < p.units;
   }
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
@@ -364,48 +443,37 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   Vals v;
   unpack_bf16(w, v);
   if (L >= 12) rope_lane<true>(v, cs);
-  float scale;
-  uint32_t ebyte, codes[8];
-  quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
 
-  // scales: one 4-byte store per block (any layout the strides describe).  A
-  // unit whose position is outside the table gets NaN scales, which turns all
-  // of its dequantized values into NaN.
-  if (unit0 + q < p.units) {
-    const bool bad = PICK_ROW(q, badk) != 0;
-    uint8_t* sc = PICK_ROW(q, sck);
-    if (FMT == RQ_SCALE_UE8M0) {
-      const uint32_t word = pack_ue8m0(ebyte, blk);
-      if (L == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
-    } else if (r == 0) {
-      reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = bad ? __builtin_nanf("") : scale;
-    }
-  }
-
-  // codes: through LDS so that each store writes a unit's 512 contiguous
-  // bytes.  8-byte granule G of unit q sits at G ^ ((((G >> 4) & 3) ^ (q & 1)) << 2),
-  // which keeps both the per-lane writes and the row reads free of bank
-  // conflicts.
-  wave_lds_sync();  // the transpose reads are done before the slice is reused
-  uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+  if constexpr (kBf16) {
+    // a unit whose position is outside the table is written as NaN
+    uint4 outv[4];
+    pack_bf16(v, outv);
+    if (PICK_ROW(q, badk) != 0) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int G = 16 * blk + r + 4 * m;
-    lds8[64 * q + (G ^ (((blk ^ (q & 1)) & 3) << 2))] = make_uint2(codes[2 * m], codes[2 * m + 1]);
+      for (int k = 0; k < 4; ++k)
+        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    }
+    store_rows_bf16(lds_wave, outv, lane, outk, ok);
+  } else {
+    float scale;
+    uint32_t ebyte, codes[8];
+    quantize_lane<OUT>(v, p.eps, scale, ebyte, codes);
+
+    // scales: one 4-byte store per block (any layout the strides describe).
+    // A unit whose position is outside the table gets NaN scales, which turns
+    // all of its dequantized values into NaN.
+    if (unit0 + q < p.units) {
+      const bool bad = PICK_ROW(q, badk) != 0;
+      uint8_t* sc = PICK_ROW(q, sck);
+      if (OUT == RQ_SCALE_UE8M0) {
+        const uint32_t word = pack_ue8m0(ebyte, blk);
+        if (L == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
+      } else if (r == 0) {
+        reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = bad ? __builtin_nanf("") : scale;
+      }
+    }
+    store_rows_fp8(lds_wave, codes, lane, outk, unit0, p.units);
   }
-  wave_lds_sync();
-  // lanes 0..31 store unit 2i, lanes 32..63 unit 2i+1 (constant indices
-  // throughout, so the base pointers stay in registers)
-  const int half = lane >> 5, j16 = lane & 31;
-  uint8_t* const base01 = half ? outk[1] : outk[0];
-  uint8_t* const base23 = half ? outk[3] : outk[2];
-  const int G0 = 2 * j16;
-  const int sw = (G0 >> 4) & 3;
-  const uint4 c01 = *reinterpret_cast<const uint4*>(lds8 + 64 * half + (G0 ^ ((sw ^ half) << 2)));
-  const uint4 c23 =
-      *reinterpret_cast<const uint4*>(lds8 + 64 * (2 + half) + (G0 ^ ((sw ^ half) << 2)));
-  if (unit0 + half < p.units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
-  if (unit0 + 2 + half < p.units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
 }
 
 struct QnrParams {
@@ -420,11 +488,54 @@ struct QnrParams {
   Magic div_hpad;
   uint32_t hq, hpad;
   float eps;
-  uint16_t* q_out;
+  uint16_t* q_out;   // bf16 form: [N, Hpad, 512]
+  uint8_t* q_fp8;    // FP8 form: codes [N, Hpad, 512] ...
+  void* q_scales;    // ... and scales [N, Hpad, 4] fp32 or [N, Hpad] UE8M0 words
+  float quant_eps;
 };
 
-// The wave with grid-wide index `wave` handles units 4*wave .. 4*wave+3.
+// RMSNorm of the lane's row ([P3] section 5), v <- (v * r) * w.  The sum of
+// squares runs in a fixed tree: chunk sums left to right, then butterflies
+// over the chunk index c = 16b + 4k + r for bit 0, 1 (lanes r^1, r^2), bit
+// 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads b^1, b^2).
 template <bool HAS_WEIGHT>
+__device__ __forceinline__ void rmsnorm_lane(Vals& v, const uint4 (&wt)[4], float eps) {
+  float ps[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float acc = v.x[k][0] * v.x[k][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
+    ps[k] = acc;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap2>(ps[k]);
+  float ss = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  ss = ss + dpp_f32<kRowHalfMirror>(ss);
+  ss = ss + dpp_f32<kRowMirror>(ss);
+  const float mean = ss * (1.0f / 512.0f);
+  const float rs = 1.0f / sqrtf(mean + eps);
+
+  if (HAS_WEIGHT) {
+    Vals wv;
+    unpack_bf16(wt, wv);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * rs) * wv.x[k][e];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * rs;
+  }
+}
+
+// The wave with grid-wide index `wave` handles units 4*wave .. 4*wave+3.
+// OUT: kOutBf16 (q_out) or RQ_SCALE_FP32 / RQ_SCALE_UE8M0 (q_fp8 + q_scales).
+template <bool HAS_WEIGHT, int OUT>
 __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15;
@@ -462,88 +573,72 @@ __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint
   load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
   transpose_rows(lds_wave, raw, lane, w);
 
-  uint4 outv[4];
-  if (live) {
-    Vals v;
-    unpack_bf16(w, v);
+  uint8_t* dst[4];
+  bool ok[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ok[k] = unit0 + k < p.units;
+    dst[k] = OUT == kOutBf16
+                 ? reinterpret_cast<uint8_t*>(p.q_out + (int64_t)(unit0 + k) * kHeadDim)
+                 : p.q_fp8 + (int64_t)(unit0 + k) * kHeadDim;
+  }
 
-    // Sum of squares in the fixed tree: chunk sums left to right, then
-    // butterflies over the chunk index c = 16q + 4k + r for bit 0, 1 (lanes
-    // r^1, r^2), bit 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads q^1, q^2).
-    float ps[4];
+  if constexpr (OUT == kOutBf16) {
+    uint4 outv[4];
+    if (live) {
+      Vals v;
+      unpack_bf16(w, v);
+      rmsnorm_lane<HAS_WEIGHT>(v, wt, p.eps);
+      if (rope) rope_lane<false>(v, cs);
+      pack_bf16(v, outv);
+      if (bad) {  // position outside the table: the head is written as NaN
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float acc = v.x[k][0] * v.x[k][0];
+        for (int k = 0; k < 4; ++k)
+          outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+      }
+    } else {  // pad head (or no unit): exact +0 ([P1] section 1)
 #pragma unroll
-      for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
-      ps[k] = acc;
+      for (int k = 0; k < 4; ++k) outv[k] = make_uint4(0u, 0u, 0u, 0u);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap2>(ps[k]);
-    float ss = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    ss = ss + dpp_f32<kRowHalfMirror>(ss);
-    ss = ss + dpp_f32<kRowMirror>(ss);
-    const float mean = ss * (1.0f / 512.0f);
-    const float rs = 1.0f / sqrtf(mean + p.eps);
-
-    if (HAS_WEIGHT) {
-      Vals wv;
-      unpack_bf16(wt, wv);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * rs) * wv.x[k][e];
+    store_rows_bf16(lds_wave, outv, lane, dst, ok);
+  } else {
+    // A pad head is a zero head, quantized like any other (codes +0, scales
+    // from quant_eps).
+    Vals v;
+    if (live) {
+      unpack_bf16(w, v);
+      rmsnorm_lane<HAS_WEIGHT>(v, wt, p.eps);
+      if (rope) rope_lane<false>(v, cs);
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * rs;
+        for (int e = 0; e < 8; ++e) v.x[k][e] = 0.0f;
     }
-    if (rope) rope_lane<false>(v, cs);
-
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t o4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 f = {v.x[k][2 * i], v.x[k][2 * i + 1]};
-        o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    float scale;
+    uint32_t ebyte, codes[8];
+    quantize_lane<OUT>(v, p.quant_eps, scale, ebyte, codes);
+    // scales of unit u at u*4 floats (FP32) or word u (UE8M0); a live head of
+    // a token whose position is outside the table gets NaN scales
+    if (unit0 + q < p.units) {
+      const bool poison = live && bad;
+      const int64_t u = unit0 + q;
+      const int blk = L >> 2;
+      if (OUT == RQ_SCALE_UE8M0) {
+        const uint32_t word = pack_ue8m0(ebyte, blk);
+        if (L == 0) static_cast<uint32_t*>(p.q_scales)[u] = poison ? 0xFFFFFFFFu : word;
+      } else if ((L & 3) == 0) {
+        static_cast<float*>(p.q_scales)[4 * u + blk] = poison ? __builtin_nanf("") : scale;
       }
-      outv[k] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
-    if (bad) {  // position outside the table: the head is written as NaN
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    }
-  } else {  // pad head (or no unit): exact +0 ([P1] section 1)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) outv[k] = make_uint4(0u, 0u, 0u, 0u);
+    store_rows_fp8(lds_wave, codes, lane, dst, unit0, p.units);
   }
-
-  // Back through LDS (same slot swizzle as the input side) so that each store
-  // writes one unit's 1 KiB; the wave's 4 units are 4 KiB of contiguous q_out.
-  wave_lds_sync();  // the transpose reads are done before the slice is reused
-  const int b = L >> 2, r = L & 3;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) lds_wave[64 * q + 16 * b + r + 4 * (m ^ b)] = outv[m];
-  wave_lds_sync();
-  const int rslot = lane ^ (((lane >> 4) & 3) << 2);
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (unit0 + k < p.units)
-      reinterpret_cast<uint4*>(p.q_out + (int64_t)(unit0 + k) * kHeadDim)[lane] =
-          lds_wave[64 * k + rslot];
 }
 
-template <bool HAS_WEIGHT>
+template <bool HAS_WEIGHT, int OUT>
 __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
   extern __shared__ uint4 lds[];
-  qnr_body<HAS_WEIGHT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
+  qnr_body<HAS_WEIGHT, OUT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
 }
 
 struct KviParams {
@@ -559,12 +654,15 @@ struct KviParams {
   Magic div_bs;
   uint32_t bs;
   uint8_t* cache;
-  int64_t block_stride;
+  int64_t block_stride;  // bytes: between blocks (records), or between rows (bf16 cache)
   float eps;
 };
 
 // The wave with grid-wide index `wave` handles tokens 4*wave .. 4*wave+3.
-template <int FMT>
+// OUT: RQ_SCALE_FP32 / RQ_SCALE_UE8M0 (a 528-byte record in the paged FP8
+// cache), or kOutBf16 (a bf16 row of the token-strided cache: slot s at
+// cache + s * block_stride bytes).
+template <int OUT>
 __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
@@ -573,7 +671,7 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
   const float* csk[4];
   int64_t posk[4];
   uint32_t badk[4];
-  uint8_t* reck[4];  // the token's 528-byte record, or nullptr: nothing to write
+  uint8_t* reck[4];  // the token's record or row, or nullptr: nothing to write
   int64_t slotk[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -592,52 +690,75 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
     csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
     reck[k] = nullptr;
     if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
-      const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
-      const uint32_t idx = (uint32_t)slotk[k] - blk_i * p.bs;
-      reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
+      if (OUT == kOutBf16) {
+        reck[k] = p.cache + slotk[k] * p.block_stride;
+      } else {
+        const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
+        const uint32_t idx = (uint32_t)slotk[k] - blk_i * p.bs;
+        reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
+      }
     }
   }
   RopeCS cs;
   load_cs(PICK_ROW(q, csk), r, cs);  // unconditional, as above
   transpose_rows(lds_wave, raw, lane, w);
-  uint8_t* const rec = PICK_ROW(q, reck);
-  // Rows with nothing to write skip the rest; no early return, so a caller
-  // that inlines this body keeps a plain if/else around it.
-  if (rec) {
-    const int d0 = lane_dim0(L);
 
+  if constexpr (OUT == kOutBf16) {
     Vals v;
     unpack_bf16(w, v);
     if (L >= 12) rope_lane<false>(v, cs);
-    float scale;
-    uint32_t ebyte, codes[8];
-    quantize_lane<FMT>(v, p.eps, scale, ebyte, codes);
-    uint32_t word = 0;
-    if (FMT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
+    uint4 outv[4];
+    pack_bf16(v, outv);
+    if (PICK_ROW(q, badk) != 0) {  // position outside the table: a NaN row
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
-    if (r == 0) {
-      // a token whose position is outside the table gets NaN scales
-      const bool bad = PICK_ROW(q, badk) != 0;
-      uint32_t tail;
-      if (FMT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
-      else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
-      *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * blk) = tail;
+      for (int k = 0; k < 4; ++k)
+        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    }
+    bool ok[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ok[k] = reck[k] != nullptr;
+    store_rows_bf16(lds_wave, outv, lane, reck, ok);
+  } else {
+    uint8_t* const rec = PICK_ROW(q, reck);
+    // Rows with nothing to write skip the rest; no early return, so a caller
+    // that inlines this body keeps a plain if/else around it.
+    if (rec) {
+      const int d0 = lane_dim0(L);
+
+      Vals v;
+      unpack_bf16(w, v);
+      if (L >= 12) rope_lane<false>(v, cs);
+      float scale;
+      uint32_t ebyte, codes[8];
+      quantize_lane<OUT>(v, p.eps, scale, ebyte, codes);
+      uint32_t word = 0;
+      if (OUT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint2*>(rec + d0 + 32 * k) = make_uint2(codes[2 * k], codes[2 * k + 1]);
+      if (r == 0) {
+        // a token whose position is outside the table gets NaN scales
+        const bool bad = PICK_ROW(q, badk) != 0;
+        uint32_t tail;
+        if (OUT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
+        else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
+        *reinterpret_cast<uint32_t*>(rec + kHeadDim + 4 * blk) = tail;
+      }
     }
   }
 }
 
-template <int FMT>
+template <int OUT>
 __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   extern __shared__ uint4 lds[];
-  kvi_body<FMT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
+  kvi_body<OUT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
 }
 
-// qnorm_rope and kv_rope_quant_insert in one launch ([P1] section 1: the op
-// normalizes and rotates q and inserts the rotated, quantized kv in a single
-// kernel).  Waves [0, q_waves) run the q path, the rest the kv path; the
-// branch is per wave, and every wave has its own LDS slice.
+// The q path and the kv path in one launch ([P1] section 1: the op
+// normalizes and rotates q and inserts the rotated kv in a single kernel;
+// section 2 names the full-cache forms: q as bf16 (in place) or FP8, kv into
+// a token-strided cache).  Waves [0, q_waves) run the q path, the rest the kv
+// path; the branch is per wave, and every wave has its own LDS slice.
 struct FusedParams {
   LaunchHdr hdr;
   QnrParams q;
@@ -648,18 +769,18 @@ struct FusedParams {
 // s_waitcnt vmcnt(0), the other counters left at their maximum (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <bool HAS_WEIGHT, int FMT>
+template <bool HAS_WEIGHT, int QOUT, int KOUT>
 __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
   extern __shared__ uint4 lds[];
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   const uint32_t w = wave_index(p.hdr);
   if (w >= p.q_waves) {
-    kvi_body<FMT>(p.k, w - p.q_waves, lds_wave);
+    kvi_body<KOUT>(p.k, w - p.q_waves, lds_wave);
     // The compiler lays the two paths out one after the other; with the kv
     // stores drained here, the q path's loads keep their per-load waits.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   } else {
-    qnr_body<HAS_WEIGHT>(p.q, w, lds_wave);
+    qnr_body<HAS_WEIGHT, QOUT>(p.q, w, lds_wave);
   }
 }
 
@@ -951,34 +1072,89 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
   return launch(fn, p.units, kIrqChunkLog2, &p, (hipStream_t)stream);
 }
 
+int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
+                  const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+                  int64_t n_tokens, int32_t n_heads, int32_t heads_per_group, uint16_t* out,
+                  int64_t out_stride_group, int64_t out_stride_token, void* stream) {
+  if (n_tokens < 0 || n_heads < 1 || heads_per_group < 1 || max_pos < 1) return RQ_ERR_SHAPE;
+  if (n_heads % heads_per_group) return RQ_ERR_SHAPE;
+  if ((int64_t)n_tokens * n_heads >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!o || !positions || !cos_sin_cache || !out) return RQ_ERR_NULL;
+  if (o_stride_token < 1 || o_stride_head < 1 || out_stride_group < 1 || out_stride_token < 1)
+    return RQ_ERR_STRIDE;
+  if (!aligned(o, 16) || (o_stride_token % 8) || (o_stride_head % 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin_cache, 16) || !aligned(out, 16) || (out_stride_group % 8) ||
+      (out_stride_token % 8))
+    return RQ_ERR_ALIGN;
+  const int64_t G = n_heads / heads_per_group;
+  {
+    const int64_t n[2] = {G, n_tokens}, s[2] = {out_stride_group, out_stride_token};
+    if (!no_overlap(2, n, s, (int64_t)heads_per_group * kHeadDim)) return RQ_ERR_STRIDE;
+  }
+  // in place only when every head's output lands on its own input row
+  if (out == o && !(o_stride_head == kHeadDim && out_stride_token == o_stride_token &&
+                    out_stride_group == (int64_t)heads_per_group * kHeadDim))
+    return RQ_ERR_STRIDE;
+  IrqParams p;
+  p.o = o; p.o_st = o_stride_token; p.o_sh = o_stride_head;
+  p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
+  p.units = (uint32_t)(n_tokens * n_heads);
+  p.div_heads = make_magic((uint32_t)n_heads);
+  p.div_hpg = make_magic((uint32_t)heads_per_group);
+  p.n_heads = (uint32_t)n_heads; p.hpg = (uint32_t)heads_per_group;
+  p.eps = 0.0f;
+  p.out = reinterpret_cast<uint8_t*>(out);
+  p.out_sg = 2 * out_stride_group; p.out_st = 2 * out_stride_token;  // bytes in the kernel
+  p.scales = nullptr; p.sc_sg = p.sc_st = p.sc_sb = 0;
+  return launch((const void*)irq_kernel<kOutBf16>, p.units, kIrqChunkLog2, &p,
+                (hipStream_t)stream);
+}
+
 }  // extern "C"
 
 namespace {
 
 // Validation and parameter set-up shared by the standalone and the fused
 // entry points.  RQ_OK with `empty` set means there is nothing to launch.
+// qout: kOutBf16 (q_out) or a scale format (q_fp8 + q_scales, quant_eps).
 int prep_qnr(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
              const uint16_t* norm_weight, const int64_t* positions, const float* cos_sin_cache,
              int64_t max_pos, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
-             double eps, uint16_t* q_out, QnrParams& p, bool& empty) {
+             double eps, int qout, uint16_t* q_out, uint8_t* q_fp8, void* q_scales,
+             double quant_eps, QnrParams& p, bool& empty) {
   empty = true;
+  const bool bf16 = qout == kOutBf16;
   if (n_tokens < 0 || n_heads_q < 1 || max_pos < 1) return RQ_ERR_SHAPE;
   if (q_head_padded < n_heads_q) return RQ_ERR_SHAPE;  // [P1] section 1 check
   if ((int64_t)n_tokens * q_head_padded >= (int64_t(1) << 31)) return RQ_ERR_SHAPE;
   if (!(eps > 0.0) || !((float)eps > 0.0f) || !((float)eps <= 3.0e38f)) return RQ_ERR_VALUE;
+  if (!bf16 && !eps_quant_ok(quant_eps)) return RQ_ERR_VALUE;
   if (n_tokens == 0) return RQ_OK;
-  if (!q_in || !positions || !cos_sin_cache || !q_out) return RQ_ERR_NULL;
+  if (!q_in || !positions || !cos_sin_cache) return RQ_ERR_NULL;
+  if (bf16 ? !q_out : (!q_fp8 || !q_scales)) return RQ_ERR_NULL;
   if (q_stride_token < 1 || q_stride_head < 1) return RQ_ERR_STRIDE;
   if (!aligned(q_in, 16) || (q_stride_token % 8) || (q_stride_head % 8) ||
-      !aligned(positions, 8) || !aligned(cos_sin_cache, 16) || !aligned(q_out, 16) ||
+      !aligned(positions, 8) || !aligned(cos_sin_cache, 16) ||
       (norm_weight && !aligned(norm_weight, 16)))
     return RQ_ERR_ALIGN;
+  if (bf16 ? !aligned(q_out, 16) : (!aligned(q_fp8, 16) || !aligned(q_scales, 4)))
+    return RQ_ERR_ALIGN;
+  // in place only when every head's output lands on its own input row
+  if (bf16 && q_out == q_in &&
+      !(q_head_padded == n_heads_q && q_stride_head == kHeadDim &&
+        q_stride_token == (int64_t)n_heads_q * kHeadDim))
+    return RQ_ERR_STRIDE;
   p.q = q_in; p.q_st = q_stride_token; p.q_sh = q_stride_head;
   p.weight = norm_weight; p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
   p.units = (uint32_t)(n_tokens * q_head_padded);
   p.div_hpad = make_magic((uint32_t)q_head_padded);
   p.hq = (uint32_t)n_heads_q; p.hpad = (uint32_t)q_head_padded;
-  p.eps = (float)eps; p.q_out = q_out;
+  p.eps = (float)eps;
+  p.q_out = bf16 ? q_out : nullptr;
+  p.q_fp8 = bf16 ? nullptr : q_fp8;
+  p.q_scales = bf16 ? nullptr : q_scales;
+  p.quant_eps = bf16 ? 0.0f : (float)quant_eps;
   empty = false;
   return RQ_OK;
 }
@@ -1011,6 +1187,54 @@ int prep_kvi(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positio
   return RQ_OK;
 }
 
+// The kv path into the token-strided bf16 cache: slot s owns the 512
+// elements at cache + s * cache_stride_token.
+int prep_kvf(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
+             const float* cos_sin_cache, int64_t max_pos, const int64_t* slot_mapping,
+             int64_t n_tokens, uint16_t* cache, int64_t num_slots, int64_t cache_stride_token,
+             KviParams& p, bool& empty) {
+  empty = true;
+  if (n_tokens < 0 || max_pos < 1 || num_slots < 1) return RQ_ERR_SHAPE;
+  if (n_tokens >= (int64_t(1) << 27)) return RQ_ERR_SHAPE;
+  if (cache_stride_token < kHeadDim) return RQ_ERR_STRIDE;
+  if (num_slots > (int64_t(1) << 62) / cache_stride_token) return RQ_ERR_SHAPE;
+  if (n_tokens == 0) return RQ_OK;
+  if (!kv || !positions || !cos_sin_cache || !slot_mapping || !cache) return RQ_ERR_NULL;
+  if (kv_stride_token < 1) return RQ_ERR_STRIDE;
+  if (!aligned(kv, 16) || (kv_stride_token % 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin_cache, 16) || !aligned(slot_mapping, 8) || !aligned(cache, 16) ||
+      (cache_stride_token % 8))
+    return RQ_ERR_ALIGN;
+  p.kv = kv; p.kv_st = kv_stride_token; p.positions = positions; p.cs = cos_sin_cache;
+  p.max_pos = max_pos; p.slots = slot_mapping; p.n_tokens = (uint32_t)n_tokens;
+  p.num_slots = num_slots;
+  p.div_bs = make_magic(1u); p.bs = 1u;  // unused by the bf16 form
+  p.cache = reinterpret_cast<uint8_t*>(cache);
+  p.block_stride = 2 * cache_stride_token;  // bytes in the kernel
+  p.eps = 0.0f;
+  empty = false;
+  return RQ_OK;
+}
+
+template <int QOUT>
+const void* qnr_fn(bool has_weight) {
+  return has_weight ? (const void*)qnr_kernel<true, QOUT> : (const void*)qnr_kernel<false, QOUT>;
+}
+
+template <int QOUT, int KOUT>
+const void* fused_fn(bool has_weight) {
+  return has_weight ? (const void*)fused_qnr_kvi_kernel<true, QOUT, KOUT>
+                    : (const void*)fused_qnr_kvi_kernel<false, QOUT, KOUT>;
+}
+
+// One grid for both paths: q waves first, then kv waves.  `launch` sizes
+// grids in 16-lane rows, 4 per wave.
+int launch_fused(const void* fn, FusedParams& p, void* stream) {
+  p.q_waves = (p.q.units + 3u) / 4u;
+  const uint32_t kv_waves = (p.k.n_tokens + 3u) / 4u;
+  return launch(fn, 4u * (p.q_waves + kv_waves), kQnrChunkLog2, &p, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1023,10 +1247,28 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
   QnrParams p;
   bool empty;
   const int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions,
-                          cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps, q_out,
-                          p, empty);
+                          cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps,
+                          kOutBf16, q_out, nullptr, nullptr, 0.0, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  const void* fn = norm_weight ? (const void*)qnr_kernel<true> : (const void*)qnr_kernel<false>;
+  return launch(qnr_fn<kOutBf16>(norm_weight != nullptr), p.units, kQnrChunkLog2, &p,
+                (hipStream_t)stream);
+}
+
+int qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+                   const uint16_t* norm_weight, const int64_t* positions,
+                   const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+                   int32_t n_heads_q, int32_t q_head_padded, double eps, int32_t scale_fmt,
+                   double quant_eps, uint8_t* q_fp8, void* q_scales, void* stream) {
+  if (scale_fmt != RQ_SCALE_FP32 && scale_fmt != RQ_SCALE_UE8M0) return RQ_ERR_VALUE;
+  QnrParams p;
+  bool empty;
+  const int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions,
+                          cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps,
+                          scale_fmt, nullptr, q_fp8, q_scales, quant_eps, p, empty);
+  if (rc != RQ_OK || empty) return rc;
+  const bool w = norm_weight != nullptr;
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? qnr_fn<RQ_SCALE_UE8M0>(w)
+                                               : qnr_fn<RQ_SCALE_FP32>(w);
   return launch(fn, p.units, kQnrChunkLog2, &p, (hipStream_t)stream);
 }
 
@@ -1047,6 +1289,19 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
   return launch(fn, p.n_tokens, kKviChunkLog2, &p, (hipStream_t)stream);
 }
 
+int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
+                        const float* cos_sin_cache, int64_t max_pos,
+                        const int64_t* slot_mapping, int64_t n_tokens, uint16_t* cache,
+                        int64_t num_slots, int64_t cache_stride_token, void* stream) {
+  KviParams p;
+  bool empty;
+  const int rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping,
+                          n_tokens, cache, num_slots, cache_stride_token, p, empty);
+  if (rc != RQ_OK || empty) return rc;
+  return launch((const void*)kvi_kernel<kOutBf16>, p.n_tokens, kKviChunkLog2, &p,
+                (hipStream_t)stream);
+}
+
 int qnorm_rope_kv_rope_quant_insert(
     const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
     const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
@@ -1058,23 +1313,59 @@ int qnorm_rope_kv_rope_quant_insert(
   FusedParams p;
   bool eq, ek;
   int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions, cos_sin_cache,
-                    max_pos, n_tokens, n_heads_q, q_head_padded, eps, q_out, p.q, eq);
+                    max_pos, n_tokens, n_heads_q, q_head_padded, eps, kOutBf16, q_out, nullptr,
+                    nullptr, 0.0, p.q, eq);
   if (rc != RQ_OK) return rc;
   rc = prep_kvi(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping, n_tokens,
                 k_cache, num_blocks, block_stride_bytes, cache_block_size, scale_fmt, quant_eps,
                 p.k, ek);
   if (rc != RQ_OK || eq) return rc;  // both are empty exactly when n_tokens == 0
-  p.q_waves = (p.q.units + 3u) / 4u;
-  const uint32_t kv_waves = (p.k.n_tokens + 3u) / 4u;
-  const void* fn;
-  if (norm_weight)
-    fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)fused_qnr_kvi_kernel<true, RQ_SCALE_UE8M0>
-                                     : (const void*)fused_qnr_kvi_kernel<true, RQ_SCALE_FP32>;
-  else
-    fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)fused_qnr_kvi_kernel<false, RQ_SCALE_UE8M0>
-                                     : (const void*)fused_qnr_kvi_kernel<false, RQ_SCALE_FP32>;
-  // `launch` sizes grids in 16-lane rows: 4 per wave
-  return launch(fn, 4u * (p.q_waves + kv_waves), kQnrChunkLog2, &p, (hipStream_t)stream);
+  const bool w = norm_weight != nullptr;
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? fused_fn<kOutBf16, RQ_SCALE_UE8M0>(w)
+                                               : fused_fn<kOutBf16, RQ_SCALE_FP32>(w);
+  return launch_fused(fn, p, stream);
+}
+
+int qnorm_rope_kv_rope_insert_full(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, uint16_t* q_out, uint16_t* cache, int64_t num_slots, int64_t cache_stride_token,
+    void* stream) {
+  FusedParams p;
+  bool eq, ek;
+  int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions, cos_sin_cache,
+                    max_pos, n_tokens, n_heads_q, q_head_padded, eps, kOutBf16, q_out, nullptr,
+                    nullptr, 0.0, p.q, eq);
+  if (rc != RQ_OK) return rc;
+  rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping, n_tokens,
+                cache, num_slots, cache_stride_token, p.k, ek);
+  if (rc != RQ_OK || eq) return rc;
+  return launch_fused(fused_fn<kOutBf16, kOutBf16>(norm_weight != nullptr), p, stream);
+}
+
+int qnorm_rope_fp8_kv_rope_insert_full(
+    const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+    const uint16_t* norm_weight, const uint16_t* kv, int64_t kv_stride_token,
+    const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
+    const int64_t* slot_mapping, int64_t n_tokens, int32_t n_heads_q, int32_t q_head_padded,
+    double eps, int32_t scale_fmt, double quant_eps, uint8_t* q_fp8, void* q_scales,
+    uint16_t* cache, int64_t num_slots, int64_t cache_stride_token, void* stream) {
+  if (scale_fmt != RQ_SCALE_FP32 && scale_fmt != RQ_SCALE_UE8M0) return RQ_ERR_VALUE;
+  FusedParams p;
+  bool eq, ek;
+  int rc = prep_qnr(q_in, q_stride_token, q_stride_head, norm_weight, positions, cos_sin_cache,
+                    max_pos, n_tokens, n_heads_q, q_head_padded, eps, scale_fmt, nullptr, q_fp8,
+                    q_scales, quant_eps, p.q, eq);
+  if (rc != RQ_OK) return rc;
+  rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping, n_tokens,
+                cache, num_slots, cache_stride_token, p.k, ek);
+  if (rc != RQ_OK || eq) return rc;
+  const bool w = norm_weight != nullptr;
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? fused_fn<RQ_SCALE_UE8M0, kOutBf16>(w)
+                                               : fused_fn<RQ_SCALE_FP32, kOutBf16>(w);
+  return launch_fused(fn, p, stream);
 }
 
 int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,

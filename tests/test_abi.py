@@ -63,6 +63,7 @@ def test_block_threads_knob():
 
 
 A = 0x100000  # fake, 256-byte aligned "device" addresses
+B = 0x900000  # a second one, for outputs that must not alias an input
 
 
 def irq(**kw):
@@ -77,7 +78,7 @@ def irq(**kw):
 
 def qnr(**kw):
     a = dict(q=A, qst=64 * 512, qsh=512, w=A, pos=A, cs=A, max_pos=8192, n=8, hq=64, hpad=128,
-             eps=1e-6, out=A)
+             eps=1e-6, out=B)
     a.update(kw)
     return _lib.lib().qnorm_rope(a["q"], a["qst"], a["qsh"], a["w"], a["pos"], a["cs"],
                                  a["max_pos"], a["n"], a["hq"], a["hpad"], a["eps"], a["out"],
@@ -134,7 +135,9 @@ def test_irq_token_major_strides_are_accepted_by_validation():
     (dict(q=None), NULL), (dict(out=None), NULL), (dict(pos=None), NULL), (dict(cs=None), NULL),
     (dict(qst=0), STRIDE),
     (dict(q=A + 2), ALIGN), (dict(qsh=500), ALIGN), (dict(w=A + 8), ALIGN),
-    (dict(out=A + 4), ALIGN), (dict(cs=A + 8), ALIGN),
+    (dict(out=B + 4), ALIGN), (dict(cs=A + 8), ALIGN),
+    (dict(out=A), STRIDE),                                # in place needs hpad == hq
+    (dict(out=A, hpad=64, qsh=1024, qst=128 * 512), STRIDE),  # ... and contiguous q
 ])
 def test_qnr_validation(kw, status):
     assert qnr(**kw) == status
@@ -156,7 +159,7 @@ def test_kvi_validation(kw, status):
 
 def fused(**kw):
     a = dict(q=A, qst=64 * 512, qsh=512, w=A, kv=A, kst=512, pos=A, cs=A, max_pos=8192,
-             slots=A, n=8, hq=64, hpad=128, eps=1e-6, out=A, cache=A, nb=256, stride=64 * 528,
+             slots=A, n=8, hq=64, hpad=128, eps=1e-6, out=B, cache=A, nb=256, stride=64 * 528,
              bs=64, fmt=0, qeps=1e-10)
     a.update(kw)
     return _lib.lib().qnorm_rope_kv_rope_quant_insert(
@@ -175,7 +178,7 @@ def test_fused_zero_tokens_is_ok_without_pointers():
     (dict(hpad=63), SHAPE), (dict(bs=0), SHAPE), (dict(eps=0.0), VALUE), (dict(qeps=0.0), VALUE),
     (dict(fmt=3), VALUE), (dict(q=None), NULL), (dict(kv=None), NULL), (dict(slots=None), NULL),
     (dict(cache=None), NULL), (dict(stride=100), STRIDE), (dict(kv=A + 8), ALIGN),
-    (dict(out=A + 8), ALIGN),
+    (dict(out=B + 8), ALIGN), (dict(out=A), STRIDE),
 ])
 def test_fused_validation(kw, status):
     assert fused(**kw) == status
@@ -208,6 +211,126 @@ def test_indexer_zero_tokens_is_ok_without_pointers():
 ])
 def test_indexer_validation(kw, status):
     assert idx(**kw) == status
+
+
+def irb(**kw):
+    a = dict(o=A, ost=32 * 512, osh=512, pos=A, cs=A, max_pos=4096, n=16, h=32, hpg=8, out=B,
+             osg=16 * 8 * 512, ost2=8 * 512)
+    a.update(kw)
+    return _lib.lib().inv_rope_bf16(a["o"], a["ost"], a["osh"], a["pos"], a["cs"], a["max_pos"],
+                                    a["n"], a["h"], a["hpg"], a["out"], a["osg"], a["ost2"], None)
+
+
+def test_irb_zero_tokens_is_ok_without_pointers():
+    assert irb(n=0, o=None, pos=None, cs=None, out=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpg=7), SHAPE), (dict(n=-1), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(o=None), NULL), (dict(out=None), NULL), (dict(pos=None), NULL),
+    (dict(ost=0), STRIDE), (dict(osg=0), STRIDE),
+    (dict(o=A + 8), ALIGN), (dict(out=B + 8), ALIGN), (dict(osg=16 * 8 * 512 + 4), ALIGN),
+    (dict(ost2=4 * 512), STRIDE),                 # token rows overlap
+    (dict(out=A), STRIDE),                        # group-major over o is not in place
+    (dict(out=A, osg=8 * 512, ost2=32 * 512, osh=1024, ost=64 * 512), STRIDE),
+])
+def test_irb_validation(kw, status):
+    assert irb(**kw) == status
+
+
+@host_only
+def test_irb_token_major_in_place_passes_validation():
+    # out == o with the token-major strides: each head overwrites its own row;
+    # without a GPU the launch itself comes back as RQ_ERR_HIP
+    assert irb(out=A, osg=8 * 512, ost2=32 * 512) == -6
+
+
+def qf8(**kw):
+    a = dict(q=A, qst=64 * 512, qsh=512, w=A, pos=A, cs=A, max_pos=8192, n=8, hq=64, hpad=128,
+             eps=1e-6, fmt=0, qeps=1e-10, codes=B, sc=B)
+    a.update(kw)
+    return _lib.lib().qnorm_rope_fp8(a["q"], a["qst"], a["qsh"], a["w"], a["pos"], a["cs"],
+                                     a["max_pos"], a["n"], a["hq"], a["hpad"], a["eps"],
+                                     a["fmt"], a["qeps"], a["codes"], a["sc"], None)
+
+
+def test_qf8_zero_tokens_is_ok_without_pointers():
+    assert qf8(n=0, q=None, w=None, pos=None, cs=None, codes=None, sc=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpad=63), SHAPE), (dict(fmt=2), VALUE), (dict(qeps=0.0), VALUE), (dict(eps=0.0), VALUE),
+    (dict(codes=None), NULL), (dict(sc=None), NULL), (dict(q=None), NULL),
+    (dict(codes=B + 8), ALIGN), (dict(sc=B + 2), ALIGN), (dict(q=A + 8), ALIGN),
+])
+def test_qf8_validation(kw, status):
+    assert qf8(**kw) == status
+
+
+def kvf(**kw):
+    a = dict(kv=A, kst=512, pos=A, cs=A, max_pos=8192, slots=A, n=8, cache=B, ns=1024, cst=512)
+    a.update(kw)
+    return _lib.lib().kv_rope_insert_full(a["kv"], a["kst"], a["pos"], a["cs"], a["max_pos"],
+                                          a["slots"], a["n"], a["cache"], a["ns"], a["cst"], None)
+
+
+def test_kvf_zero_tokens_is_ok_without_pointers():
+    assert kvf(n=0, kv=None, pos=None, cs=None, slots=None, cache=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(ns=0), SHAPE), (dict(n=-2), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(ns=1 << 60), SHAPE),
+    (dict(cst=504), STRIDE), (dict(kst=0), STRIDE),
+    (dict(kv=None), NULL), (dict(slots=None), NULL), (dict(cache=None), NULL),
+    (dict(cache=B + 8), ALIGN), (dict(cst=516), ALIGN), (dict(slots=A + 4), ALIGN),
+])
+def test_kvf_validation(kw, status):
+    assert kvf(**kw) == status
+
+
+def fused_full(fp8=False, **kw):
+    a = dict(q=A, qst=64 * 512, qsh=512, w=A, kv=A, kst=512, pos=A, cs=A, max_pos=8192,
+             slots=A, n=8, hq=64, hpad=128, eps=1e-6, out=B, fmt=0, qeps=1e-10, sc=B,
+             cache=B + 0x100000, ns=1024, cst=512)
+    a.update(kw)
+    L = _lib.lib()
+    if fp8:
+        return L.qnorm_rope_fp8_kv_rope_insert_full(
+            a["q"], a["qst"], a["qsh"], a["w"], a["kv"], a["kst"], a["pos"], a["cs"],
+            a["max_pos"], a["slots"], a["n"], a["hq"], a["hpad"], a["eps"], a["fmt"], a["qeps"],
+            a["out"], a["sc"], a["cache"], a["ns"], a["cst"], None)
+    return L.qnorm_rope_kv_rope_insert_full(
+        a["q"], a["qst"], a["qsh"], a["w"], a["kv"], a["kst"], a["pos"], a["cs"], a["max_pos"],
+        a["slots"], a["n"], a["hq"], a["hpad"], a["eps"], a["out"], a["cache"], a["ns"],
+        a["cst"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_fused_full_zero_tokens_is_ok_without_pointers(fp8):
+    assert fused_full(fp8, n=0, q=None, w=None, kv=None, pos=None, cs=None, slots=None,
+                      out=None, sc=None, cache=None) == OK
+
+
+@host_only
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(hpad=63), SHAPE), (dict(ns=0), SHAPE), (dict(eps=0.0), VALUE),
+    (dict(q=None), NULL), (dict(kv=None), NULL), (dict(cache=None), NULL),
+    (dict(cst=100), STRIDE), (dict(kv=A + 8), ALIGN), (dict(out=B + 8), ALIGN),
+])
+def test_fused_full_validation(fp8, kw, status):
+    assert fused_full(fp8, **kw) == status
+
+
+@host_only
+def test_fused_full_fp8_scale_format_checked():
+    assert fused_full(True, fmt=7) == VALUE
+    assert fused_full(True, qeps=0.0) == VALUE
+    assert fused_full(True, sc=None) == NULL
 
 
 def test_python_binding_rejects_host_tensors():
