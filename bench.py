@@ -1,6 +1,7 @@
 """Benchmark of the fused RoPE + block-FP8 hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only irq|qnr|kvi|decode|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--only irq|qnr|kvi|idx|variants|decode|copy]
 
 A step is one launch of ``inv_rope_fp8_quant`` over the prefill workload
 (16384 tokens x 32 heads in 4 groups of 8, head dim 512, bf16 in, e4m3 +
@@ -11,8 +12,10 @@ line reports achieved HBM throughput over the algorithmic bytes, tokens/s,
 the roofline fraction against the 8 TB/s HBM3E peak, HBM traffic from
 rocprofv3 counters when they were taken on the current kernel source, and
 the CPU oracle timed on this host.  The other ops (qnorm_rope and
-kv_rope_quant_insert on the forward workload, and decode latencies) are timed
-the same way and reported under "extra".
+kv_rope_quant_insert on the forward workload, their one-launch fusion, the
+indexer query path, the output variants - bf16 inverse RoPE, q to FP8, kv into
+the bf16 token-strided cache and the fused full-cache forms - and decode
+latencies) are timed the same way and reported under "extra".
 """
 import argparse
 import hashlib
@@ -39,6 +42,10 @@ KERNEL_SRC = os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", "ropequant.hip")
 #     + 8 + 256 B.
 #   indexer_q_rope_quant per (token, head): 256 B read + 128 B codes + 8 B of
 #     weights; per token 8 + 256 B.
+#   inv_rope_bf16 per (token, head): 1024 B read + 1024 B write; per token 8 + 256 B.
+#   qnorm_rope_fp8 per live head: 1024 B read; per head (live or pad): 512 B
+#     codes + 16 B scales; per token 8 + 256 B; plus the 1024 B weight once.
+#   kv_rope_insert_full per token: 1024 B read + 1024 B row + 8 B slot + 8 + 256 B.
 
 
 def irq_bytes(N, H, fmt="fp32"):
@@ -57,6 +64,22 @@ def idx_bytes(N, H):
     # per (token, head): 256 B bf16 read + 128 B codes + 4 B weight in + 4 B out;
     # per token: 8 B position + 256 B cos/sin row
     return N * H * (256 + 128 + 4 + 4) + N * (8 + 256)
+
+
+def irb_bytes(N, H):
+    return N * H * 2048 + N * 264
+
+
+def qf8_bytes(N, Hq, Hpad):
+    return N * Hq * 1024 + N * Hpad * (512 + 16) + N * 264 + 1024
+
+
+def kvf_bytes(N):
+    return N * (1024 + 1024 + 8 + 264)
+
+
+def _rate(name, us, b):
+    return dict(workload=name, us=us, bytes=b, gbs=b / us / 1e3, frac=b / us / 1e3 / HBM_PEAK_GBS)
 
 
 def kernel_hash():
@@ -164,6 +187,57 @@ def bench_qnr_kvi(args, device, stream):
         b = idx_bytes(N, H)
         res["indexer_q_rope_quant"] = dict(workload="idx_n4096_h64_d128", us=ms * 1e3, bytes=b,
                                            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+    return res
+
+
+def bench_variants(args, device, stream):
+    """The output variants on the same workloads as their quantized forms."""
+    import torch
+
+    import rope_fp8_quant_amd as rq
+    from rope_fp8_quant_amd import synth
+    res = {}
+    cfg = synth.IRQ_PREFILL
+    o, pos, cache = synth.irq_inputs(cfg)
+    N, H, hpg = cfg["N"], cfg["H"], cfg["hpg"]
+    od, pd, cd = to_dev(o, device), to_dev(pos, device), to_dev(cache, device)
+    del o
+    out = torch.empty((H // hpg, N, hpg * 512), dtype=torch.bfloat16, device=device)
+    ms = time_launches(lambda: rq.inv_rope_bf16(od, pd, cd, hpg, out), args.steps, args.warmup,
+                       stream)
+    res["inv_rope_bf16"] = _rate(cfg["name"], ms * 1e3, irb_bytes(N, H))
+    del od, out
+    torch.cuda.empty_cache()
+
+    qc, kc = synth.QNR_FORWARD, synth.KVI_FORWARD
+    q, w, pos, cache = synth.qnr_inputs(qc)
+    kv, _, slots, _ = synth.kvi_inputs(kc)
+    N, Hq, Hpad = qc["N"], qc["Hq"], qc["Hpad"]
+    qd, wd, pd, cd, kd, sd = (to_dev(x, device) for x in (q, w, pos, cache, kv, slots))
+    del q
+    codes, sc = rq.empty_qnorm_rope_fp8_outputs(N, Hpad, device)
+    ms = time_launches(lambda: rq.qnorm_rope_fp8(qd, wd, pd, cd, codes, sc, qc["eps"]),
+                       args.steps, args.warmup, stream)
+    res["qnorm_rope_fp8"] = _rate(qc["name"], ms * 1e3, qf8_bytes(N, Hq, Hpad))
+    ns = kc["num_blocks"] * kc["block_size"]
+    full = torch.empty((ns, 512), dtype=torch.bfloat16, device=device)
+    ms = time_launches(lambda: rq.kv_rope_insert_full(kd, pd, cd, sd, full), args.steps,
+                       args.warmup, stream)
+    res["kv_rope_insert_full"] = _rate(f"kvf_forward_n{N}_{ns}slots", ms * 1e3, kvf_bytes(N))
+    ms = time_launches(
+        lambda: rq.qnorm_rope_fp8_kv_rope_insert_full(qd, wd, kd, pd, cd, sd, codes, sc, full,
+                                                      qc["eps"]),
+        args.steps, args.warmup, stream)
+    res["qnorm_rope_fp8_kv_rope_insert_full"] = _rate(
+        "qnr_forward (fp8) + kvf_forward, one launch", ms * 1e3,
+        qf8_bytes(N, Hq, Hpad) + kvf_bytes(N) - N * 264)
+    # bf16 full-cache form in place: q_head_padded == Hq, q_out is q_in
+    ms = time_launches(
+        lambda: rq.qnorm_rope_kv_rope_insert_full(qd, wd, kd, pd, cd, sd, qd, full, qc["eps"]),
+        args.steps, args.warmup, stream)
+    res["qnorm_rope_kv_rope_insert_full"] = _rate(
+        f"q in place n{N}_h{Hq} + kvf_forward, one launch", ms * 1e3,
+        N * Hq * 2048 + N * 264 + 1024 + kvf_bytes(N) - N * 264)
     return res
 
 
@@ -275,7 +349,7 @@ def main():
     # from idle, so the timed region starts after 100 untimed launches
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "decode", "copy"],
+    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "variants", "decode", "copy"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -301,6 +375,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({"decode": bench_decode(args, device, stream)}))
         return
+    if args.only == "variants":
+        print(json.dumps({"extra": bench_variants(args, device, stream)}))
+        return
 
     cfg, ms, host_inputs = bench_irq(args, device, stream)
     N, H = cfg["N"], cfg["H"]
@@ -314,6 +391,8 @@ def main():
             us=ms_ue * 1e3, gbs=irq_bytes(N, H, "ue8m0") / ms_ue / 1e6)
         torch.cuda.empty_cache()
         extra.update(bench_qnr_kvi(args, device, stream))
+        torch.cuda.empty_cache()
+        extra.update(bench_variants(args, device, stream))
         torch.cuda.empty_cache()
         extra["decode"] = bench_decode(args, device, stream)
     line = {

@@ -36,6 +36,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <atomic>
+#include <cstring>
 
 #include "ropequant.h"
 
@@ -144,6 +145,13 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
 template <typename T>
 __device__ __forceinline__ T load_uniform(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// 16-byte nontemporal store: the output rows are not read again by this
+// kernel, and for whole 1 KiB rows it measured faster than a plain store.
+__device__ __forceinline__ void store_nt(uint8_t* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (__attribute__((address_space(1))) u32x4_t*)p);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -311,7 +319,7 @@ __device__ __forceinline__ void store_rows_bf16(uint4* lds_wave, const uint4 (&o
   const int rslot = lane ^ (((lane >> 4) & 3) << 2);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    if (ok[k]) reinterpret_cast<uint4*>(dst[k])[lane] = lds_wave[64 * k + rslot];
+    if (ok[k]) store_nt(dst[k] + 16 * lane, lds_wave[64 * k + rslot]);
 }
 
 // e4m3 codes (chunk m in codes[2m], codes[2m+1]): each store writes one
@@ -492,14 +500,16 @@ struct QnrParams {
   uint8_t* q_fp8;    // FP8 form: codes [N, Hpad, 512] ...
   void* q_scales;    // ... and scales [N, Hpad, 4] fp32 or [N, Hpad] UE8M0 words
   float quant_eps;
+  float pad_scale;     // a zero head's block scale: quant_eps / 448, or its UE8M0 power of two
+  uint32_t pad_ebyte;  // a zero head's UE8M0 exponent byte
 };
 
-// RMSNorm of the lane's row ([P3] section 5), v <- (v * r) * w.  The sum of
-// squares runs in a fixed tree: chunk sums left to right, then butterflies
-// over the chunk index c = 16b + 4k + r for bit 0, 1 (lanes r^1, r^2), bit
-// 2, 3 (this lane's k^1, k^2), bit 4, 5 (quads b^1, b^2).
-template <bool HAS_WEIGHT>
-__device__ __forceinline__ void rmsnorm_lane(Vals& v, const uint4 (&wt)[4], float eps) {
+// RMSNorm of the lane's row ([P3] section 5), v <- (v * r) * w, in two
+// steps.  rms_inv: r = 1 / sqrt(mean(v^2) + eps), the sum of squares in a
+// fixed tree: chunk sums left to right, then butterflies over the chunk index
+// c = 16b + 4k + r for bit 0, 1 (lanes r^1, r^2), bit 2, 3 (this lane's k^1,
+// k^2), bit 4, 5 (quads b^1, b^2).
+__device__ __forceinline__ float rms_inv(const Vals& v, float eps) {
   float ps[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -516,8 +526,14 @@ __device__ __forceinline__ void rmsnorm_lane(Vals& v, const uint4 (&wt)[4], floa
   ss = ss + dpp_f32<kRowHalfMirror>(ss);
   ss = ss + dpp_f32<kRowMirror>(ss);
   const float mean = ss * (1.0f / 512.0f);
-  const float rs = 1.0f / sqrtf(mean + eps);
+  return 1.0f / sqrtf(mean + eps);
+}
 
+// v <- (v * rs) * w with the lane's weight chunks already in registers
+// (HAS_WEIGHT), or v <- v * rs.
+template <bool HAS_WEIGHT>
+__device__ __forceinline__ void rmsnorm_lane(Vals& v, const uint4 (&wt)[4], float eps) {
+  const float rs = rms_inv(v, eps);
   if (HAS_WEIGHT) {
     Vals wv;
     unpack_bf16(wt, wv);
@@ -525,6 +541,32 @@ __device__ __forceinline__ void rmsnorm_lane(Vals& v, const uint4 (&wt)[4], floa
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v.x[k][e] = (v.x[k][e] * rs) * wv.x[k][e];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.x[k][e] = v.x[k][e] * rs;
+  }
+}
+
+// The same, reading the lane's weight chunks (cached) only here, pair by pair:
+// fewer registers live across the kernel, for the heavier FP8 form.
+template <bool HAS_WEIGHT>
+__device__ __forceinline__ void rmsnorm_lane_late_weight(Vals& v, const uint16_t* wrow,
+                                                         float eps) {
+  const float rs = rms_inv(v, eps);
+  if (HAS_WEIGHT) {
+    const uint4* wp = reinterpret_cast<const uint4*>(wrow);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 wk = wp[4 * k];
+      const uint32_t d[4] = {wk.x, wk.y, wk.z, wk.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v.x[k][2 * i] = (v.x[k][2 * i] * rs) * bf_lo(d[i]);
+        v.x[k][2 * i + 1] = (v.x[k][2 * i + 1] * rs) * bf_hi(d[i]);
+      }
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -561,16 +603,22 @@ __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint
   const bool bad = pos < 0 || pos >= p.max_pos;
   const bool rope = L >= 12;
   const int d0 = lane_dim0(L);
-  // weight and cos/sin are read by every lane (cached): unconditional loads
-  // keep the memory counters' order fixed
+  // bf16 form: weight and cos/sin are read by every lane (cached) before the
+  // transpose, so their latency hides behind it (unconditional loads keep the
+  // memory counters' order fixed).  The FP8 form, which holds more registers,
+  // reads them where they are used: it measured faster with the higher
+  // occupancy that buys, the bf16 form slower.
+  const float* csrow = p.cs + (bad ? 0 : pos) * 64;
   uint4 wt[4];
-  if (HAS_WEIGHT) {
-    const uint4* wp = reinterpret_cast<const uint4*>(p.weight + d0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) wt[k] = wp[4 * k];
-  }
   RopeCS cs;
-  load_cs(p.cs + (bad ? 0 : pos) * 64, L & 3, cs);
+  if constexpr (OUT == kOutBf16) {
+    if (HAS_WEIGHT) {
+      const uint4* wp = reinterpret_cast<const uint4*>(p.weight + d0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) wt[k] = wp[4 * k];
+    }
+    load_cs(csrow, L & 3, cs);
+  }
   transpose_rows(lds_wave, raw, lane, w);
 
   uint8_t* dst[4];
@@ -602,22 +650,19 @@ __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint
     }
     store_rows_bf16(lds_wave, outv, lane, dst, ok);
   } else {
-    // A pad head is a zero head, quantized like any other (codes +0, scales
-    // from quant_eps).
-    Vals v;
+    // A pad head is a zero head, quantized like any other: codes +0 and the
+    // scales of a block whose amax is quant_eps, which the host computed with
+    // the same fp32 operations.  Only live heads run the arithmetic.
+    float scale = p.pad_scale;
+    uint32_t ebyte = p.pad_ebyte, codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if (live) {
+      Vals v;
       unpack_bf16(w, v);
-      rmsnorm_lane<HAS_WEIGHT>(v, wt, p.eps);
+      rmsnorm_lane_late_weight<HAS_WEIGHT>(v, HAS_WEIGHT ? p.weight + d0 : nullptr, p.eps);
+      load_cs(csrow, L & 3, cs);
       if (rope) rope_lane<false>(v, cs);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v.x[k][e] = 0.0f;
+      quantize_lane<OUT>(v, p.quant_eps, scale, ebyte, codes);
     }
-    float scale;
-    uint32_t ebyte, codes[8];
-    quantize_lane<OUT>(v, p.quant_eps, scale, ebyte, codes);
     // scales of unit u at u*4 floats (FP32) or word u (UE8M0); a live head of
     // a token whose position is outside the table gets NaN scales
     if (unit0 + q < p.units) {
@@ -1155,6 +1200,23 @@ int prep_qnr(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head
   p.q_fp8 = bf16 ? nullptr : q_fp8;
   p.q_scales = bf16 ? nullptr : q_scales;
   p.quant_eps = bf16 ? 0.0f : (float)quant_eps;
+  // a zero head's scale, by quantize_lane's own steps (fp32 division, exact
+  // power-of-two rounding); host fp32 arithmetic is IEEE round-to-nearest
+  p.pad_scale = 0.0f;
+  p.pad_ebyte = 0u;
+  if (!bf16) {
+    const float t = p.quant_eps / kE4m3Max;
+    if (qout == RQ_SCALE_UE8M0) {
+      uint32_t u;
+      std::memcpy(&u, &t, 4);
+      const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
+      const uint32_t sb = (uint32_t)(kexp + 127) << 23;
+      std::memcpy(&p.pad_scale, &sb, 4);
+      p.pad_ebyte = (uint32_t)(kexp + 127);
+    } else {
+      p.pad_scale = t;
+    }
+  }
   empty = false;
   return RQ_OK;
 }

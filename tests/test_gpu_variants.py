@@ -163,6 +163,23 @@ def test_qf8_decode_sizes(N):
     qf8_check(q, w, pos, cache, 128, "fp32", "decode")
 
 
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+@pytest.mark.parametrize("quant_eps", [2.0 ** -116, 1e-10, 1e-4, 3.0, 1000.0])
+def test_qf8_pad_only_waves_take_the_zero_head_scales(scale_fmt, quant_eps):
+    # Hq = 4, Hpad = 12: two of every three waves hold pad heads only, and
+    # their scales come from the host; both kinds must match the oracle
+    cfg = dict(synth.QNR_FORWARD, N=9, Hq=4, Hpad=12, seed=125)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    print(f"[case] qnorm_rope_fp8 pad waves eps={quant_eps} {scale_fmt}", flush=True)
+    codes, sc = rq.empty_qnorm_rope_fp8_outputs(9, 12, DEV, scale_fmt)
+    rq.qnorm_rope_fp8(dev(q), dev(w), dev(pos), dev(cache), codes, sc, 1e-6, scale_fmt,
+                      quant_eps)
+    torch.cuda.synchronize()
+    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, 12, 1e-6, FMT[scale_fmt], quant_eps)
+    assert_bits_equal(host(sc), es, "pad-wave scales")
+    assert_codes_match(host(codes), ec, "pad-wave codes")
+
+
 def test_qf8_strided_input():
     cfg = dict(synth.QNR_FORWARD, N=19, Hq=6, Hpad=8, seed=120)
     q, w, pos, cache = synth.qnr_inputs(cfg)
