@@ -102,6 +102,26 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(stop) / steps  # ms per launch
 
 
+# MI355X's MALL (last-level cache) holds 256 MB: a config whose working set
+# is smaller is timed cycling through enough copies of its buffers that every
+# launch touches data last used more than ROTATE_BYTES of traffic earlier.
+ROTATE_BYTES = 600 * (1 << 20)
+
+
+def rotation_sets(set_bytes):
+    return max(1, -(-ROTATE_BYTES // int(set_bytes)))
+
+
+def time_rotating(fns, steps, warmup, stream):
+    """time_launches over a list of equivalent launches on distinct buffers."""
+    it = [0]
+
+    def step():
+        fns[it[0] % len(fns)]()
+        it[0] += 1
+    return time_launches(step, steps, warmup, stream)
+
+
 def to_dev(a, device):
     import torch
     a = np.ascontiguousarray(a)
@@ -151,12 +171,16 @@ def bench_qnr_kvi(args, device, stream):
         kv, pos, slots, cache = synth.kvi_inputs(cfg)
         kd, pd, sd, cd = (to_dev(x, device) for x in (kv, pos, slots, cache))
         k_cache = rq.empty_kv_cache(cfg["num_blocks"], cfg["block_size"], device, fill=0xAA)
-        ms = time_launches(
-            lambda: rq.kv_rope_quant_insert(kd, pd, cd, sd, k_cache, cfg["block_size"]),
-            args.steps, args.warmup, stream)
         b = kvi_bytes(cfg["N"])
+        sets = rotation_sets(kd.nbytes + k_cache.nbytes)
+        rot = [(kd.clone(), sd.clone(), k_cache.clone()) for _ in range(sets)]
+        fns = [lambda k=k, s=s, c=c: rq.kv_rope_quant_insert(k, pd, cd, s, c, cfg["block_size"])
+               for k, s, c in rot]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
         res["kv_rope_quant_insert"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
-                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS,
+                                           buffer_sets=sets)
+        del rot, fns
         # the same q and kv work in one launch (positions 0..8191 serve both)
         qc = synth.QNR_FORWARD
         q, w, qpos, qcache = synth.qnr_inputs(qc)
@@ -179,14 +203,34 @@ def bench_qnr_kvi(args, device, stream):
         qd, wd = to_dev(q, device), to_dev(w, device)
         pd = to_dev(np.arange(N, dtype=np.int64), device)
         cd = to_dev(synth.cos_sin_cache(N), device)
-        q_fp8 = torch.empty((N, H, 128), dtype=torch.uint8, device=device)
-        wo = torch.empty((N, H), dtype=torch.float32, device=device)
-        ms = time_launches(
-            lambda: rq.indexer_q_rope_quant(qd, pd, cd, wd, q_fp8, wo, 128 ** -0.5),
-            args.steps, args.warmup, stream)
         b = idx_bytes(N, H)
+        sets = rotation_sets(b)
+        rot = [(qd.clone(), wd.clone(), torch.empty((N, H, 128), dtype=torch.uint8, device=device),
+                torch.empty((N, H), dtype=torch.float32, device=device)) for _ in range(sets)]
+        fns = [lambda q=q, w=w, o=o, x=x: rq.indexer_q_rope_quant(q, pd, cd, w, o, x, 128 ** -0.5)
+               for q, w, o, x in rot]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
         res["indexer_q_rope_quant"] = dict(workload="idx_n4096_h64_d128", us=ms * 1e3, bytes=b,
-                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS)
+                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS,
+                                           buffer_sets=sets)
+        del rot, fns
+        # irregular grouping: 4096 tokens x 48 heads in groups of 6
+        cfg = synth.IRQ_IRREGULAR
+        o, pos, cache = synth.irq_inputs(cfg)
+        N, H, hpg = cfg["N"], cfg["H"], cfg["hpg"]
+        od, pd, cd = to_dev(o, device), to_dev(pos, device), to_dev(cache, device)
+        del o
+        b = irq_bytes(N, H)
+        sets = rotation_sets(b)
+        rot = [(od.clone(),) + rq.empty_inv_rope_fp8_quant_outputs(N, H, hpg, device)
+               for _ in range(sets)]
+        fns = [lambda x=x, out=out, sc=sc: rq.inv_rope_fp8_quant(x, pd, cd, hpg, out, sc)
+               for x, out, sc in rot]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
+        res["inv_rope_fp8_quant_irregular"] = dict(
+            workload=cfg["name"], us=ms * 1e3, bytes=b, gbs=b / ms / 1e6,
+            frac=b / ms / 1e6 / HBM_PEAK_GBS, buffer_sets=sets)
+        del rot, fns, od
     return res
 
 
@@ -221,9 +265,13 @@ def bench_variants(args, device, stream):
     res["qnorm_rope_fp8"] = _rate(qc["name"], ms * 1e3, qf8_bytes(N, Hq, Hpad))
     ns = kc["num_blocks"] * kc["block_size"]
     full = torch.empty((ns, 512), dtype=torch.bfloat16, device=device)
-    ms = time_launches(lambda: rq.kv_rope_insert_full(kd, pd, cd, sd, full), args.steps,
-                       args.warmup, stream)
-    res["kv_rope_insert_full"] = _rate(f"kvf_forward_n{N}_{ns}slots", ms * 1e3, kvf_bytes(N))
+    sets = rotation_sets(kd.nbytes + full.nbytes)
+    rot = [(kd.clone(), torch.empty_like(full)) for _ in range(sets)]
+    fns = [lambda k=k, f=f: rq.kv_rope_insert_full(k, pd, cd, sd, f) for k, f in rot]
+    ms = time_rotating(fns, args.steps, args.warmup, stream)
+    res["kv_rope_insert_full"] = dict(_rate(f"kvf_forward_n{N}_{ns}slots", ms * 1e3,
+                                            kvf_bytes(N)), buffer_sets=sets)
+    del rot, fns
     ms = time_launches(
         lambda: rq.qnorm_rope_fp8_kv_rope_insert_full(qd, wd, kd, pd, cd, sd, codes, sc, full,
                                                       qc["eps"]),
@@ -268,14 +316,34 @@ def graph_per_call_us(fn, calls=100, replays=5):
     return times[len(times) // 2]
 
 
+def cold_single_us(fn, scratch, reps=21):
+    """One launch on its own, timed with events right around it, after a 1 GiB
+    write has flushed the caches (median over reps)."""
+    import torch
+    times = []
+    for _ in range(reps):
+        scratch.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
 def bench_decode(args, device, stream):
-    """Decode sizes: per call through Python (host-bound) and in a HIP graph."""
+    """Decode sizes: per call through Python (host-bound), in a HIP graph
+    (GPU-side cost with warm caches), and one cold launch on its own."""
     import torch
 
     import rope_fp8_quant_amd as rq
     from rope_fp8_quant_amd import synth
     res = {}
     cache = to_dev(synth.cos_sin_cache(65536), device)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=device)
     for N in synth.DECODE_NS:
         cfg = dict(synth.IRQ_TINY, N=N, H=32, hpg=8, max_pos=65536, seed=40 + N)
         o, pos, _ = synth.irq_inputs(cfg)
@@ -293,10 +361,14 @@ def bench_decode(args, device, stream):
         ms = time_launches(irq, 200, 20, stream)
         msq = time_launches(qnr, 200, 20, stream)
         gi, gq = graph_per_call_us(irq), graph_per_call_us(qnr)
+        ci, cq = cold_single_us(irq, scratch), cold_single_us(qnr, scratch)
         res[f"N{N}"] = dict(irq_us_python=round(ms * 1e3, 2), irq_us_graph=round(gi, 2),
                             irq_gbs_graph=round(irq_bytes(N, 32) / gi / 1e3, 1),
+                            irq_us_single_cold=round(ci, 2),
                             qnr_us_python=round(msq * 1e3, 2), qnr_us_graph=round(gq, 2),
-                            qnr_gbs_graph=round(qnr_bytes(N, 32, 128) / gq / 1e3, 1))
+                            qnr_gbs_graph=round(qnr_bytes(N, 32, 128) / gq / 1e3, 1),
+                            qnr_us_single_cold=round(cq, 2))
+    del scratch
     return res
 
 
@@ -329,6 +401,63 @@ def cpu_baseline(irq_inputs, budget_s=12.0):
                 tokens_per_s=round(n2 / dt, 1),
                 sample=f"first {n2} of {N} tokens x {H} heads of the same workload, one "
                        f"thread, {dt:.1f} s")
+
+
+def _oracle_shard(spec):
+    """Worker of the sharded CPU baseline (a fresh process): the same oracle
+    call on one token range of the shared inputs; returns its compute time."""
+    from multiprocessing import shared_memory
+
+    import oracle
+    (o_name, o_shape, c_name, c_shape, pos, lo, hi) = spec
+    so = shared_memory.SharedMemory(name=o_name)
+    sc = shared_memory.SharedMemory(name=c_name)
+    try:
+        o = np.ndarray(o_shape, dtype=np.uint16, buffer=so.buf)
+        cache = np.ndarray(c_shape, dtype=np.float32, buffer=sc.buf)
+        mine = np.ascontiguousarray(o[lo:hi])
+        oracle.lib()
+        t = time.perf_counter()
+        oracle.inv_rope_fp8_quant(mine, pos, cache, 8)
+        return time.perf_counter() - t
+    finally:
+        del o, cache
+        so.close()
+        sc.close()
+
+
+def cpu_baseline_sharded(irq_inputs):
+    """The same oracle on every host core of this GPU's share, tokens split
+    evenly; the slowest shard's compute time is the run's time."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    o, pos, cache = irq_inputs
+    N, H = o.shape[0], o.shape[1]
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    workers = max(1, min(16, ncpu))
+    so = shared_memory.SharedMemory(create=True, size=o.nbytes)
+    sc = shared_memory.SharedMemory(create=True, size=cache.nbytes)
+    try:
+        np.ndarray(o.shape, dtype=np.uint16, buffer=so.buf)[:] = o
+        np.ndarray(cache.shape, dtype=np.float32, buffer=sc.buf)[:] = cache
+        cuts = [N * i // workers for i in range(workers + 1)]
+        specs = [(so.name, o.shape, sc.name, cache.shape, pos[a:b].copy(), a, b)
+                 for a, b in zip(cuts[:-1], cuts[1:])]
+        with mp.get_context("spawn").Pool(workers) as pool:
+            times = pool.map(_oracle_shard, specs)
+    finally:
+        so.close()
+        so.unlink()
+        sc.close()
+        sc.unlink()
+    dt = max(times)
+    return dict(value=round(irq_bytes(N, H) / dt / 1e9, 4), unit="GB/s", cores=workers,
+                kind="oracle", tokens_per_s=round(N / dt, 1),
+                sample=f"all {N} tokens x {H} heads split over {workers} processes, "
+                       f"slowest shard {dt:.2f} s")
 
 
 def traffic_from_profile():
@@ -419,6 +548,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(host_inputs)
+        line["cpu_baseline_sharded"] = cpu_baseline_sharded(host_inputs)
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)
