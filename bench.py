@@ -82,6 +82,10 @@ def _rate(name, us, b):
     return dict(workload=name, us=us, bytes=b, gbs=b / us / 1e3, frac=b / us / 1e3 / HBM_PEAK_GBS)
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -403,6 +407,15 @@ def cpu_baseline(irq_inputs, budget_s=12.0):
                        f"thread, {dt:.1f} s")
 
 
+def _oracle_shard_proc(spec, results):
+    """Process body of the sharded CPU baseline: runs one shard and reports its
+    compute time (or the error) through `results`, then exits normally."""
+    try:
+        results.put(_oracle_shard(spec))
+    except Exception as e:  # reported to the parent, which raises
+        results.put(f"{type(e).__name__}: {e}")
+
+
 def _oracle_shard(spec):
     """Worker of the sharded CPU baseline (a fresh process): the same oracle
     call on one token range of the shared inputs; returns its compute time."""
@@ -446,8 +459,19 @@ def cpu_baseline_sharded(irq_inputs):
         cuts = [N * i // workers for i in range(workers + 1)]
         specs = [(so.name, o.shape, sc.name, cache.shape, pos[a:b].copy(), a, b)
                  for a, b in zip(cuts[:-1], cuts[1:])]
-        with mp.get_context("spawn").Pool(workers) as pool:
-            times = pool.map(_oracle_shard, specs)
+        # one process per shard, each exiting on its own once done (no
+        # terminate(): a profiler attached to the children may not survive it)
+        ctx = mp.get_context("spawn")
+        results = ctx.SimpleQueue()
+        procs = [ctx.Process(target=_oracle_shard_proc, args=(sp, results)) for sp in specs]
+        for pr in procs:
+            pr.start()
+        times = [results.get() for _ in procs]
+        for pr in procs:
+            pr.join()
+        bad = [t for t in times if not isinstance(t, float)]
+        if bad:
+            raise RuntimeError(f"sharded oracle failed: {bad[0]}")
     finally:
         so.close()
         so.unlink()
@@ -515,14 +539,18 @@ def main():
     extra = {}
     if args.only is None:
         torch.cuda.empty_cache()
+        progress("headline done; ue8m0")
         _, ms_ue, _ = bench_irq(args, device, stream, "ue8m0")
         extra["inv_rope_fp8_quant_ue8m0"] = dict(
             us=ms_ue * 1e3, gbs=irq_bytes(N, H, "ue8m0") / ms_ue / 1e6)
         torch.cuda.empty_cache()
+        progress("qnr / kvi / fused / indexer / irregular")
         extra.update(bench_qnr_kvi(args, device, stream))
         torch.cuda.empty_cache()
+        progress("output variants")
         extra.update(bench_variants(args, device, stream))
         torch.cuda.empty_cache()
+        progress("decode")
         extra["decode"] = bench_decode(args, device, stream)
     line = {
         "metric": "achieved HBM GB/s (% of peak) + tokens/s, inv_rope_fp8_quant 16k tok x 32 heads",
@@ -547,7 +575,9 @@ def main():
                      "traffic": traffic_from_profile()},
     }
     if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle, one thread)")
         line["cpu_baseline"] = cpu_baseline(host_inputs)
+        progress("cpu baseline (oracle, sharded)")
         line["cpu_baseline_sharded"] = cpu_baseline_sharded(host_inputs)
     if extra:
         line["extra"] = extra

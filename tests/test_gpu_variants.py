@@ -308,3 +308,68 @@ def test_fused_full_fp8_matches_oracle_and_separate_calls(scale_fmt, N, Hq, hpad
     assert_codes_match(res[0][0], ec, "fused fp8 codes")
     exp = oracle.kv_rope_insert_full(kv, pos, cache, slots, np.full((ns, 512), 0xAAAA, np.uint16))
     assert_bits_equal(res[0][2], exp, "fused fp8 kv rows")
+
+
+# ----------------------------------------------------- graph capture
+
+def test_graph_replays_of_the_other_entry_points_match_eager():
+    # inv_rope_bf16, qnorm_rope_fp8, kv_rope_insert_full, the fused ops and
+    # the indexer captured in one HIP graph, replayed four times with eager
+    # scribbles over every output in between.  Slots are a permutation of all
+    # cache rows, so every output byte is rewritten by each replay.
+    N = 24
+    o, pos, cache = synth.irq_inputs(dict(synth.IRQ_TINY, N=N, H=16, hpg=4, seed=160))
+    q, w, qpos, qcache = synth.qnr_inputs(dict(synth.QNR_FORWARD, N=N, Hq=8, Hpad=12, seed=161))
+    kv = synth.normal_bf16((N, 512), 162, synth.T_KV)
+    slots = synth.slot_permutation(N, N, 162)
+    iq = synth.normal_bf16((N, 8, 128), 163, synth.T_Q)
+    iw = np.random.default_rng([163, 9]).uniform(0, 1, (N, 8)).astype(np.float32)
+    od, pd, cd = dev(o), dev(pos), dev(cache)
+    qd, wd, qpd, qcd = dev(q), dev(w), dev(qpos), dev(qcache)
+    kd, sd, iqd, iwd = dev(kv), dev(slots), dev(iq), dev(iw)
+    bf = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    outs = dict(
+        irb=bf(4, N, 4 * 512),
+        qf8_codes=torch.empty((N, 12, 512), dtype=torch.uint8, device=DEV),
+        qf8_sc=torch.empty((N, 12, 4), dtype=torch.float32, device=DEV),
+        kvf=bf(N, 512),
+        fq=bf(N, 12, 512),
+        fk=torch.empty((3, 8 * 528), dtype=torch.uint8, device=DEV),
+        ffc=torch.empty((N, 12, 512), dtype=torch.uint8, device=DEV),
+        ffs=torch.empty((N, 12), dtype=torch.int32, device=DEV),
+        ffk=bf(N, 512),
+        iq8=torch.empty((N, 8, 128), dtype=torch.uint8, device=DEV),
+        iwo=torch.empty((N, 8), dtype=torch.float32, device=DEV),
+    )
+
+    def step():
+        rq.inv_rope_bf16(od, pd, cd, 4, outs["irb"])
+        rq.qnorm_rope_fp8(qd, wd, qpd, qcd, outs["qf8_codes"], outs["qf8_sc"], 1e-6)
+        rq.kv_rope_insert_full(kd, qpd, qcd, sd, outs["kvf"])
+        rq.qnorm_rope_kv_rope_quant_insert(qd, wd, kd, qpd, qcd, sd, outs["fq"], outs["fk"], 8)
+        rq.qnorm_rope_fp8_kv_rope_insert_full(qd, wd, kd, qpd, qcd, sd, outs["ffc"], outs["ffs"],
+                                              outs["ffk"], 1e-6, "ue8m0")
+        rq.indexer_q_rope_quant(iqd, qpd, qcd, iwd, outs["iq8"], outs["iwo"], 128 ** -0.5)
+
+    print("[case] graph of every other entry point", flush=True)
+    step()
+    torch.cuda.synchronize()
+    eager = {k: host(t).copy() for k, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs.values():  # eager work between replays
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, t in outs.items():
+            assert_bits_equal(host(t), eager[k], f"replay {rep} {k}")
+    # and the eager results are the oracle's
+    assert_bits_equal(eager["irb"], oracle.inv_rope_bf16(o, pos, cache, 4), "graph irb")
+    exp = oracle.kv_rope_insert_full(kv, qpos, qcache, slots, np.zeros((N, 512), np.uint16))
+    assert_bits_equal(eager["kvf"], exp, "graph kvf")
