@@ -39,6 +39,7 @@
 #include <cstring>
 
 #include "ropequant.h"
+#include "exact_div.h"
 
 namespace {
 
@@ -241,15 +242,16 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
   m = __builtin_fmaxf(m, eps);
   float mult;
   if (FMT == RQ_SCALE_UE8M0) {
-    const float t = m / kE4m3Max;
+    const float t = m < __builtin_inff() ? div448(m) : m;
     const uint32_t u = __builtin_bit_cast(uint32_t, t);
     const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
     scale = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
     mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
     ebyte = (uint32_t)(kexp + 127);
   } else {
-    scale = m / kE4m3Max;
-    mult = 1.0f / scale;
+    const bool finite = m < __builtin_inff();
+    scale = finite ? div448(m) : m;
+    mult = finite ? recip_scale(scale) : 0.0f;
     ebyte = 0;
   }
 #pragma unroll
@@ -526,7 +528,10 @@ __device__ __forceinline__ float rms_inv(const Vals& v, float eps) {
   ss = ss + dpp_f32<kRowHalfMirror>(ss);
   ss = ss + dpp_f32<kRowMirror>(ss);
   const float mean = ss * (1.0f / 512.0f);
-  return 1.0f / sqrtf(mean + eps);
+  // 1 / sqrt, each correctly rounded: sqrtf is the compiler's exact square
+  // root; the reciprocal of its result (a normal below 2^64, as the argument
+  // is at least the smallest positive fp32) is recip_scale, exact there
+  return recip_scale(sqrtf(mean + eps));
 }
 
 // v <- (v * rs) * w with the lane's weight chunks already in registers
@@ -942,7 +947,7 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
     m = __builtin_fmaxf(m, dpp_f32<kRowHalfMirror>(m));
     m = __builtin_fmaxf(m, dpp_f32<kRowMirror>(m));
     m = __builtin_fmaxf(m, p.eps);
-    const uint32_t tb = __builtin_bit_cast(uint32_t, m / kE4m3Max);
+    const uint32_t tb = __builtin_bit_cast(uint32_t, m < __builtin_inff() ? div448(m) : m);
     const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
     const float qs = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
     const float mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
