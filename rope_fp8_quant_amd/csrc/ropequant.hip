@@ -90,6 +90,9 @@ constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
 constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within the row
+constexpr int kRowShl4 = 0x104;       // lane i <- lane i+4 within the row
+constexpr int kRowShl8 = 0x108;       // lane i <- lane i+8 within the row
+constexpr int kRowShl12 = 0x10C;      // lane i <- lane i+12 within the row
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -330,7 +333,10 @@ __device__ __forceinline__ void store_rows_bf16(uint4* lds_wave, const uint4 (&o
 // and the row reads free of bank conflicts.  Lanes 0..31 store units 0 and 2,
 // lanes 32..63 units 1 and 3 (constant indices throughout, so the base
 // pointers stay in scalar registers).  Unit k is stored when
-// unit0 + k < units (a tail wave past the last unit stores nothing).
+// unit0 + k < units (a tail wave past the last unit stores nothing).  NT:
+// nontemporal stores, faster for the q path's rows (half of them pad rows)
+// and slower for inv_rope_fp8_quant's, as measured.
+template <bool NT>
 __device__ __forceinline__ void store_rows_fp8(uint4* lds_wave, const uint32_t (&codes)[8],
                                                int lane, uint8_t* const (&dst)[4],
                                                uint32_t unit0, uint32_t units) {
@@ -351,8 +357,13 @@ __device__ __forceinline__ void store_rows_fp8(uint4* lds_wave, const uint32_t (
   const uint4 c01 = *reinterpret_cast<const uint4*>(lds8 + 64 * half + (G0 ^ ((sw ^ half) << 2)));
   const uint4 c23 =
       *reinterpret_cast<const uint4*>(lds8 + 64 * (2 + half) + (G0 ^ ((sw ^ half) << 2)));
-  if (unit0 + half < units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
-  if (unit0 + 2 + half < units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
+  if (NT) {
+    if (unit0 + half < units) store_nt(base01 + 16 * j16, c01);
+    if (unit0 + 2 + half < units) store_nt(base23 + 16 * j16, c23);
+  } else {
+    if (unit0 + half < units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
+    if (unit0 + 2 + half < units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
+  }
 }
 
 // Launch shape, filled in by the host: every params struct starts with it.
@@ -384,6 +395,7 @@ struct IrqParams {
   int64_t out_sg, out_st;
   void* scales;
   int64_t sc_sg, sc_st, sc_sb;
+  uint32_t sc_vec4;  // FP32 scales of a head contiguous and 16-byte aligned
 };
 
 // Row q of the wave picks its value out of the four wave-uniform ones.
@@ -469,20 +481,35 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     uint32_t ebyte, codes[8];
     quantize_lane<OUT>(v, p.eps, scale, ebyte, codes);
 
-    // scales: one 4-byte store per block (any layout the strides describe).
-    // A unit whose position is outside the table gets NaN scales, which turns
-    // all of its dequantized values into NaN.
+    // scales.  A unit whose position is outside the table gets NaN scales,
+    // which turns all of its dequantized values into NaN.  FP32 scales laid
+    // out four to a head (the group-major and token-major layouts) are
+    // gathered into the row's first lane and written with one nontemporal
+    // 16-byte store: the per-block 4-byte stores of 16 lanes, through the
+    // cache, measured 3.5% slower over the whole kernel.  Other layouts
+    // (MN-major) take one 4-byte store per block.
     if (unit0 + q < p.units) {
       const bool bad = PICK_ROW(q, badk) != 0;
       uint8_t* sc = PICK_ROW(q, sck);
       if (OUT == RQ_SCALE_UE8M0) {
         const uint32_t word = pack_ue8m0(ebyte, blk);
         if (L == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
-      } else if (r == 0) {
-        reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = bad ? __builtin_nanf("") : scale;
+      } else {
+        const float sv = bad ? __builtin_nanf("") : scale;
+        if (p.sc_vec4) {
+          // block b's scale sits in quad b: lanes 4, 8, 12 of the row
+          const float s1 = dpp_f32<kRowShl4>(sv);
+          const float s2 = dpp_f32<kRowShl8>(sv);
+          const float s3 = dpp_f32<kRowShl12>(sv);
+          if (L == 0)
+            store_nt(sc, make_uint4(__builtin_bit_cast(uint32_t, sv), __builtin_bit_cast(uint32_t, s1),
+                                    __builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, s3)));
+        } else if (r == 0) {
+          reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = sv;
+        }
       }
     }
-    store_rows_fp8(lds_wave, codes, lane, outk, unit0, p.units);
+    store_rows_fp8<false>(lds_wave, codes, lane, outk, unit0, p.units);
   }
 }
 
@@ -681,7 +708,7 @@ __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint
         static_cast<float*>(p.q_scales)[4 * u + blk] = poison ? __builtin_nanf("") : scale;
       }
     }
-    store_rows_fp8(lds_wave, codes, lane, dst, unit0, p.units);
+    store_rows_fp8<true>(lds_wave, codes, lane, dst, unit0, p.units);
   }
 }
 
@@ -861,7 +888,6 @@ struct IdxParams {
   int64_t wo_st;
 };
 
-constexpr int kRowShl4 = 0x104;  // lane i <- lane i+4 within the row
 constexpr int kRowShr4 = 0x114;  // lane i <- lane i-4 within the row
 constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 4)
 
@@ -1117,6 +1143,8 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
   p.eps = (float)eps;
   p.out = out; p.out_sg = out_stride_group; p.out_st = out_stride_token;
   p.scales = scales; p.sc_sg = sc_stride_group; p.sc_st = sc_stride_token; p.sc_sb = sc_stride_block;
+  p.sc_vec4 = scale_fmt == RQ_SCALE_FP32 && sc_stride_block == 1 && sc_stride_group % 4 == 0 &&
+              sc_stride_token % 4 == 0 && aligned(scales, 16);
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)irq_kernel<RQ_SCALE_FP32>;
   return launch(fn, p.units, kIrqChunkLog2, &p, (hipStream_t)stream);
@@ -1156,7 +1184,7 @@ int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_he
   p.eps = 0.0f;
   p.out = reinterpret_cast<uint8_t*>(out);
   p.out_sg = 2 * out_stride_group; p.out_st = 2 * out_stride_token;  // bytes in the kernel
-  p.scales = nullptr; p.sc_sg = p.sc_st = p.sc_sb = 0;
+  p.scales = nullptr; p.sc_sg = p.sc_st = p.sc_sb = 0; p.sc_vec4 = 0;
   return launch((const void*)irq_kernel<kOutBf16>, p.units, kIrqChunkLog2, &p,
                 (hipStream_t)stream);
 }

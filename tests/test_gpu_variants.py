@@ -373,3 +373,24 @@ def test_graph_replays_of_the_other_entry_points_match_eager():
     assert_bits_equal(eager["irb"], oracle.inv_rope_bf16(o, pos, cache, 4), "graph irb")
     exp = oracle.kv_rope_insert_full(kv, qpos, qcache, slots, np.zeros((N, 512), np.uint16))
     assert_bits_equal(eager["kvf"], exp, "graph kvf")
+
+
+@pytest.mark.parametrize("threads", [64, 256])
+def test_irq_scales_at_a_4_byte_offset(threads):
+    # FP32 scales that are 4- but not 16-byte aligned take the per-block
+    # stores; the default-aligned ones take the gathered 16-byte store
+    rq.set_block_threads(threads)
+    cfg = dict(synth.IRQ_TINY, N=23, H=16, hpg=8, max_pos=65536, seed=170)
+    o, pos, cache = synth.irq_inputs(cfg)
+    N, G, hpg = 23, 2, 8
+    print(f"[case] irq scales at +4 bytes threads={threads}", flush=True)
+    out = torch.full((G, N, hpg * 512), 0xCD, dtype=torch.uint8, device=DEV)
+    raw = torch.full((G * N * hpg * 4 + 1,), -7.0, dtype=torch.float32, device=DEV)
+    sc = raw[1:].view(G, N, hpg * 4)
+    assert sc.data_ptr() % 16 == 4
+    rq.inv_rope_fp8_quant(dev(o), dev(pos), dev(cache), hpg, out, sc)
+    torch.cuda.synchronize()
+    eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, hpg)
+    assert_bits_equal(host(sc), es, "offset scales")
+    assert host(raw)[0] == np.float32(-7.0)
+    assert_codes_match(host(out), eo, "offset codes")
