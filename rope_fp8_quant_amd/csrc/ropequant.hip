@@ -1,37 +1,44 @@
 // libropequant: gfx950 kernels and the C ABI for the fused RoPE + block-FP8
-// steps around 512-dim attention heads.
+// steps around 512-dim attention heads, and the sparse-attention indexer's
+// 128-dim query path.
 //
 // Sources (web pages; cited by title and section):
 //   [P1] "vLLM DeepSeek-V4 성능 최적화: Eager Break 시 Workspace 재사용 개선"
 //        (analysis of vLLM PR #49236), section 1: the q-norm/RoPE + kv
-//        RoPE/quant/insert op, its caller-allocated q_out and its checks.
+//        RoPE/quant/insert op, its caller-allocated q_out and its checks;
+//        section 2: the op schema and the full-cache forms beside it.
 //   [P3] "vLLM, DeepSeek V4 모델의 저지연을 위한 RMSNorm과 라우터 GEMV 연산
 //        융합으로 성능 극대화" (analysis of vLLM PR #41263), section 5: RMSNorm.
 //   [P4] "한 프로그램이 4개 head를 처리하게 하라: DeepSeek-V4 inverse RoPE +
 //        FP8 quant 커널 3.5배 가속기" (analysis of vLLM PR #63540): intro,
 //        sections 1-4 (heads per program, partner kept in registers, block
-//        amax, launch shape by program count).
+//        amax, the compile keys and the launch shape by program count).
+//   [P5] "vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput
+//        향상" (analysis of vLLM PR #46862), section 1: the indexer query path.
 //
-// Work decomposition (all three kernels)
-//   A "unit" is one 512-dim head vector: (token, head) for inv_rope_fp8_quant
-//   and qnorm_rope, a token for kv_rope_quant_insert.  One unit is handled by
-//   one 16-lane DPP row of a wave64, so a wave holds 4 units and every
-//   cross-lane step stays inside a row.  Lane L of the row (quad q = L >> 2,
-//   r = L & 3) owns the four 8-dim chunks 16q + r + 4k (k = 0..3), i.e. dims
+// Work decomposition (the 512-dim kernels; the indexer's is described at
+// its kernel)
+//   A "unit" is one 512-dim head vector: (token, head) for inv_rope_* and
+//   qnorm_rope*, a token for the kv paths.  One unit is handled by one 16-lane
+//   DPP row of a wave64, so a wave holds 4 units and every cross-lane step
+//   stays inside a row.  Lane L of the row (quad q = L >> 2, r = L & 3) owns
+//   the four 8-dim chunks 16q + r + 4k (k = 0..3), i.e. dims
 //   [128q + 8r + 32k, +8): all 32 of its dims lie in quant block q, so a
 //   block's amax is a max over 32 registers and two quad DPP steps, and each
-//   lane divides once per block.  Every GPT-J pair (2i, 2i+1) sits in one
-//   lane as the low/high halves of a bf16 dword, so the RoPE partner never
-//   leaves its register ([P4] section 2's point, with no split/join at all).
-//   The rotated dims 448..511 are chunks k = 2, 3 of lanes 12..15.
+//   lane computes its block's scale once.  Every GPT-J pair (2i, 2i+1) sits
+//   in one lane as the low/high halves of a bf16 dword, so the RoPE partner
+//   never leaves its register ([P4] section 2's point, with no split/join at
+//   all).  The rotated dims 448..511 are chunks k = 2, 3 of lanes 12..15.
 //   The pages group heads per program so that a program never straddles a
 //   wo_a group ([P4] section 1); here each row computes its own
 //   (group, head-in-group) address, so a wave may mix groups or tokens and
 //   ragged head counts need no special case.
 //
-// Arithmetic: IEEE binary32 basic operations, round to nearest even, no FMA
-// (built with -ffp-contract=off), correctly rounded divide and sqrt (the
-// compiler's default expansion), fp32 denormals preserved.
+// Arithmetic: IEEE binary32 basic operations, round to nearest even, no
+// contraction (built with -ffp-contract=off); the square root is the
+// compiler's correctly rounded one; m / 448 and 1 / s come from the exact
+// FMA forms of exact_div.h; fp32 denormals are preserved.  Results therefore
+// match an unfused fp32 evaluation bit for bit.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -866,9 +873,13 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
 // One 128-dim indexer head per 16-lane row, lane L holding dims [8L, 8L+8)
 // as one 16-byte load, so a wave's load instruction reads 4 whole heads
 // (1 KiB, contiguous when heads are).  A wave takes 4 * kIdxRounds heads in
-// kIdxRounds rounds and issues all rounds' reads first.  Rotate-half pairs (i, i+32) sit 4 lanes
-// apart (lanes 0..3 hold dims 0..31, lanes 4..7 dims 32..63): two DPP row
-// shifts bring each lane its partner's 8 values.
+// kIdxRounds rounds and issues all rounds' reads first.  Rotate-half pairs
+// (i, i+32) sit 4 lanes apart (lanes 0..3 hold dims 0..31, lanes 4..7 dims
+// 32..63): two DPP row shifts bring each lane its partner's 8 values.
+// Measured over rotating buffers, the kernel is bound by its per-head VALU
+// work (8 values per lane carry each head's reductions and index math), not
+// by bytes in flight: more rounds per wave, late per-round loads and scalar
+// positions were all slower.
 struct IdxParams {
   LaunchHdr hdr;
   const uint16_t* q;
@@ -889,7 +900,7 @@ struct IdxParams {
 };
 
 constexpr int kRowShr4 = 0x114;  // lane i <- lane i-4 within the row
-constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 4)
+constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 4, 8)
 
 __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
   const int lane = threadIdx.x & 63;
