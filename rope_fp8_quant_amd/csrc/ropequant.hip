@@ -870,16 +870,16 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
 
 // ---------------------------------------------------- indexer query path
 
-// One 128-dim indexer head per 16-lane row, lane L holding dims [8L, 8L+8)
-// as one 16-byte load, so a wave's load instruction reads 4 whole heads
-// (1 KiB, contiguous when heads are).  A wave takes 4 * kIdxRounds heads in
-// kIdxRounds rounds and issues all rounds' reads first.  Rotate-half pairs
-// (i, i+32) sit 4 lanes apart (lanes 0..3 hold dims 0..31, lanes 4..7 dims
-// 32..63): two DPP row shifts bring each lane its partner's 8 values.
-// Measured over rotating buffers, the kernel is bound by its per-head VALU
-// work (8 values per lane carry each head's reductions and index math), not
-// by bytes in flight: more rounds per wave, late per-round loads and scalar
-// positions were all slower.
+// One 128-dim indexer head per 16-lane row.  Lane L holds dims [4L, 4L+4)
+// (the rotated half, dims 0..63) and [64+4L, 64+4L+4) (passed through), read
+// as two 8-byte loads, so every load instruction covers whole 128-byte halves
+// of 4 heads.  Rotate-half pairs (i, i+32) then sit in lanes L and L^8: one
+// DPP row rotation by 8 brings each lane its partner's 4 values, and all 16
+// lanes rotate 4 values each (a layout with 8 consecutive dims per lane left
+// half the lanes idle through the rotation and took 31% more VALU
+// instructions; this one measured 5.7% faster).  A wave takes 4 * kIdxRounds
+// heads in kIdxRounds rounds and issues all rounds' reads first.  More rounds
+// per wave, late per-round loads and scalar positions were all slower.
 struct IdxParams {
   LaunchHdr hdr;
   const uint16_t* q;
@@ -899,82 +899,85 @@ struct IdxParams {
   int64_t wo_st;
 };
 
-constexpr int kRowShr4 = 0x114;  // lane i <- lane i-4 within the row
 constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 4, 8)
+
+constexpr int kRowRor8 = 0x128;  // lane i <- lane i^8 within the row (rotate by 8 of 16)
+
+__device__ __forceinline__ uint2 load_nt8(const uint16_t* p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load((__attribute__((address_space(1))) const u32x2_t*)p);
+  return make_uint2(v.x, v.y);
+}
 
 __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, L = lane & 15;
   const uint32_t unit0 = wave_index(p.hdr) * (4u * kIdxRounds);
-  uint4 raw[kIdxRounds];
+  // lane L holds dims [4L, 4L+4) (part A, dims 0..63) and [64+4L, 64+4L+4)
+  // (part B, passed through): two 8-byte reads, each instruction covering
+  // whole 128-byte halves of 4 heads
+  uint2 ra[kIdxRounds], rb[kIdxRounds];
   uint32_t tj[kIdxRounds], hj[kIdxRounds];
-  const uint4* rowp[kIdxRounds];
+  const uint16_t* rowp[kIdxRounds];
 #pragma unroll
   for (int j = 0; j < kIdxRounds; ++j) {
     // (a tail wave repeats the last unit; units past the end store nothing)
     const uint32_t u = min(unit0 + 4u * j + q, p.units - 1u);
     tj[j] = magic_div(u, p.div_heads);
     hj[j] = u - tj[j] * p.n_heads;
-    rowp[j] = reinterpret_cast<const uint4*>(p.q + (int64_t)tj[j] * p.q_st +
-                                             (int64_t)hj[j] * p.q_sh) + L;
+    rowp[j] = p.q + (int64_t)tj[j] * p.q_st + (int64_t)hj[j] * p.q_sh + 4 * L;
   }
   int64_t pos[kIdxRounds];
 #pragma unroll
   for (int j = 0; j < kIdxRounds; ++j) pos[j] = p.positions[tj[j]];
 #pragma unroll
-  for (int j = 0; j < kIdxRounds; ++j) raw[j] = load_nt(rowp[j]);
-  // cos/sin for this lane's 8 frequencies i = 8(L & 3) + e, and the weight
-  float4 cv[kIdxRounds][2], sv[kIdxRounds][2];
+  for (int j = 0; j < kIdxRounds; ++j) {
+    ra[j] = load_nt8(rowp[j]);
+    rb[j] = load_nt8(rowp[j] + 64);
+  }
+  // cos/sin of the lane's 4 frequencies f = 4 (L & 7) + e, and the weight
+  float4 cv[kIdxRounds], sv[kIdxRounds];
   float wgt[kIdxRounds];
   bool badj[kIdxRounds];
 #pragma unroll
   for (int j = 0; j < kIdxRounds; ++j) {
     badj[j] = pos[j] < 0 || pos[j] >= p.max_pos;
     const float4* row = reinterpret_cast<const float4*>(p.cs + (badj[j] ? 0 : pos[j]) * 64);
-    cv[j][0] = row[2 * (L & 3)];
-    cv[j][1] = row[2 * (L & 3) + 1];
-    sv[j][0] = row[8 + 2 * (L & 3)];
-    sv[j][1] = row[8 + 2 * (L & 3) + 1];
+    cv[j] = row[L & 7];
+    sv[j] = row[8 + (L & 7)];
     wgt[j] = p.w[(int64_t)tj[j] * p.w_st + hj[j]];
   }
 
 #pragma unroll
   for (int j = 0; j < kIdxRounds; ++j) {
-    // partner dwords: lanes 0..3 take lane L+4's, lanes 4..7 lane L-4's
-    const uint32_t own[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-    uint32_t par[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t up = dpp_u32<kRowShl4>(own[i]);
-      const uint32_t dn = dpp_u32<kRowShr4>(own[i]);
-      par[i] = (L & 4) ? dn : up;
-    }
+    // rotate-half pairs (i, i+32): lanes 0..7 hold i = 4L + e, lanes 8..15
+    // hold i + 32; the partner's part A is one row rotation by 8 away
+    const uint32_t par0 = dpp_u32<kRowRor8>(ra[j].x);
+    const uint32_t par1 = dpp_u32<kRowRor8>(ra[j].y);
+    const uint32_t pw[2] = {par0, par1}, ow[2] = {ra[j].x, ra[j].y};
+    const float c4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+    const float s4[4] = {sv[j].x, sv[j].y, sv[j].z, sv[j].w};
+    // r0 = x_i c - x_{i+32} s (lanes 0..7), r1 = x_{i+32} c + x_i s (lanes
+    // 8..15): own * c + partner * s', s' = -s on lanes 0..7 (negating a
+    // rounded product is exact); each result rounded to bf16 and back
+    const bool first = L < 8;
     float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf_lo(own[i]);
-      x[2 * i + 1] = bf_hi(own[i]);
-    }
-    if (L < 8) {
-      // r0 = x_i c - x_{i+32} s (lanes 0..3), r1 = x_{i+32} c + x_i s (lanes
-      // 4..7): own * c + partner * s', with s' = -s on lanes 0..3 (negating
-      // a rounded product is exact), then rounded to bf16 and back
-      const float c8[8] = {cv[j][0].x, cv[j][0].y, cv[j][0].z, cv[j][0].w,
-                           cv[j][1].x, cv[j][1].y, cv[j][1].z, cv[j][1].w};
-      const float s8[8] = {sv[j][0].x, sv[j][0].y, sv[j][0].z, sv[j][0].w,
-                           sv[j][1].x, sv[j][1].y, sv[j][1].z, sv[j][1].w};
-      const bool first = L < 4;
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = bf_lo(par[i]), p1 = bf_hi(par[i]);
-        const float s0 = first ? -s8[2 * i] : s8[2 * i];
-        const float s1 = first ? -s8[2 * i + 1] : s8[2 * i + 1];
-        const float y0 = x[2 * i] * c8[2 * i] + p0 * s0;
-        const float y1 = x[2 * i + 1] * c8[2 * i + 1] + p1 * s1;
-        x[2 * i] = (float)(__bf16)y0;
-        x[2 * i + 1] = (float)(__bf16)y1;
+      for (int h = 0; h < 2; ++h) {
+        const int e = 2 * i + h;
+        const float own = h ? bf_hi(ow[i]) : bf_lo(ow[i]);
+        const float prt = h ? bf_hi(pw[i]) : bf_lo(pw[i]);
+        const float sg = first ? -s4[e] : s4[e];
+        const float y = own * c4[e] + prt * sg;
+        x[e] = (float)(__bf16)y;
       }
     }
+    x[4] = bf_lo(rb[j].x);
+    x[5] = bf_hi(rb[j].x);
+    x[6] = bf_lo(rb[j].y);
+    x[7] = bf_hi(rb[j].y);
     // per-head amax over the row, power-of-two scale ([P5] section 1)
     float m = 0.0f;
 #pragma unroll
@@ -999,12 +1002,9 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
       code[h] = (uint32_t)wd;
     }
     if (unit0 + 4u * j + q < p.units) {
-      // nontemporal: measured 2.7% faster than a plain store here
-      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t c2 = {code[0], code[1]};
-      __builtin_nontemporal_store(
-          c2, (__attribute__((address_space(1))) u32x2_t*)(p.out + (int64_t)tj[j] * p.out_st +
-                                                           (int64_t)hj[j] * p.out_sh + 8 * L));
+      uint8_t* orow = p.out + (int64_t)tj[j] * p.out_st + (int64_t)hj[j] * p.out_sh;
+      __builtin_nontemporal_store(code[0], (__attribute__((address_space(1))) uint32_t*)(orow + 4 * L));
+      __builtin_nontemporal_store(code[1], (__attribute__((address_space(1))) uint32_t*)(orow + 64 + 4 * L));
       if (L == 0) {
         // fold the scale into the weight, left to right as printed; a head
         // whose position is outside the table gets a NaN weight
