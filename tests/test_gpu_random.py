@@ -1,0 +1,189 @@
+"""Seeded random sweeps of every op against the oracle, and stream ordering.
+
+Each case draws its shape, grouping, strides (padded rows), scale format,
+positions, slot holes and launch shape from a seeded generator, runs the HIP
+path through the C ABI and compares with the oracle to the parity bar.  The
+case parameters are printed before each GPU step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_fp8_quant_amd as rq
+from rope_fp8_quant_amd import synth
+from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("fp32", "ue8m0")
+FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
+THREADS = (0, 64, 128, 256)
+
+
+@pytest.fixture(autouse=True)
+def _table_launch():
+    rq.set_block_threads(0)
+    yield
+    rq.set_block_threads(0)
+
+
+def padded(a, pad_elems, seed):
+    """A device copy of a [N, H, D] or [N, D] array inside a wider buffer
+    (rows padded by pad_elems), returned as the strided view."""
+    t = dev(a)
+    if pad_elems == 0:
+        return t
+    shape = list(t.shape)
+    shape[-1] += pad_elems
+    big = torch.zeros(shape, dtype=t.dtype, device=DEV)
+    big[..., :t.shape[-1]] = t
+    return big[..., :t.shape[-1]]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_irq_random(case):
+    rng = np.random.default_rng([200, case])
+    hpg = int(rng.choice([1, 2, 3, 4, 6, 8, 12]))
+    G = int(rng.integers(1, 6))
+    N = int(rng.integers(1, 300))
+    fmt = FMTS[case % 2]
+    thr = THREADS[case % 4]
+    pad = int(rng.choice([0, 8, 64]))
+    max_pos = int(rng.choice([64, 4096, 65536]))
+    print(f"[case] irq random #{case}: N={N} H={G * hpg} hpg={hpg} fmt={fmt} threads={thr} "
+          f"pad={pad} max_pos={max_pos}", flush=True)
+    rq.set_block_threads(thr)
+    o = synth.normal_bf16((N, G * hpg, 512), 210 + case, synth.T_O, outlier_frac=0.01)
+    pos = rng.integers(0, max_pos, N).astype(np.int64)
+    cache = synth.cos_sin_cache(max_pos)
+    out, sc = rq.empty_inv_rope_fp8_quant_outputs(N, G * hpg, hpg, DEV, fmt)
+    rq.inv_rope_fp8_quant(padded(o, pad, case), dev(pos), dev(cache), hpg, out, sc, fmt)
+    torch.cuda.synchronize()
+    eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, hpg, FMT[fmt])
+    assert_bits_equal(host(sc), es, "random irq scales")
+    assert_codes_match(host(out), eo, "random irq codes")
+    # the bf16 form on the same inputs
+    ob = torch.empty((G, N, hpg * 512), dtype=torch.bfloat16, device=DEV)
+    rq.inv_rope_bf16(padded(o, pad, case), dev(pos), dev(cache), hpg, ob)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(ob), oracle.inv_rope_bf16(o, pos, cache, hpg), "random irb")
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_q_paths_random(case):
+    rng = np.random.default_rng([300, case])
+    N = int(rng.integers(1, 200))
+    Hq = int(rng.integers(1, 20))
+    Hpad = Hq + int(rng.choice([0, 1, 3, 8, 20]))
+    thr = THREADS[case % 4]
+    fmt = FMTS[case % 2]
+    pad = int(rng.choice([0, 8, 136]))
+    weighted = bool(case % 3)
+    eps = float(rng.choice([1e-6, 1e-3, 0.5]))
+    print(f"[case] q paths random #{case}: N={N} Hq={Hq} Hpad={Hpad} fmt={fmt} threads={thr} "
+          f"pad={pad} weight={weighted} eps={eps}", flush=True)
+    rq.set_block_threads(thr)
+    q = synth.normal_bf16((N, Hq, 512), 310 + case, synth.T_Q, std=float(rng.uniform(0.1, 4)))
+    w = synth.uniform_bf16((512,), 310 + case, synth.T_W, 0.5, 1.5) if weighted else None
+    pos = rng.integers(0, 65536, N).astype(np.int64)
+    cache = synth.cos_sin_cache(65536)
+    qd = padded(q, pad, case)
+    wd = None if w is None else dev(w)
+    q_out = torch.full((N, Hpad, 512), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    rq.qnorm_rope(qd, wd, dev(pos), dev(cache), q_out, eps)
+    codes, sc = rq.empty_qnorm_rope_fp8_outputs(N, Hpad, DEV, fmt)
+    rq.qnorm_rope_fp8(qd, wd, dev(pos), dev(cache), codes, sc, eps, fmt)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(q_out), oracle.qnorm_rope(q, w, pos, cache, Hpad, eps), "random qnr")
+    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, Hpad, eps, FMT[fmt])
+    assert_bits_equal(host(sc), es, "random qf8 scales")
+    assert_codes_match(host(codes), ec, "random qf8 codes")
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_kv_paths_random(case):
+    rng = np.random.default_rng([400, case])
+    N = int(rng.integers(1, 400))
+    bs = int(rng.choice([1, 4, 16, 64]))
+    nb = -(-(N + int(rng.integers(0, 50))) // bs)
+    fmt = FMTS[case % 2]
+    thr = THREADS[case % 4]
+    gap = int(rng.choice([0, 16, 528]))
+    pad = int(rng.choice([0, 8]))
+    print(f"[case] kv paths random #{case}: N={N} blocks={nb}x{bs} fmt={fmt} threads={thr} "
+          f"gap={gap} pad={pad}", flush=True)
+    rq.set_block_threads(thr)
+    kv = synth.normal_bf16((N, 512), 410 + case, synth.T_KV)
+    pos = rng.integers(0, 4096, N).astype(np.int64)
+    slots = synth.slot_permutation(N, nb * bs, 410 + case)
+    slots[rng.random(N) < 0.1] = -1
+    cache = synth.cos_sin_cache(4096)
+    stride = bs * 528 + gap
+    k_cache = torch.full((nb, stride), 0xAA, dtype=torch.uint8, device=DEV)
+    rq.kv_rope_quant_insert(padded(kv, pad, case), dev(pos), dev(cache), dev(slots), k_cache, bs,
+                            fmt)
+    row = 512 + int(rng.choice([0, 8, 64]))
+    full = torch.full((nb * bs, row), -21846, dtype=torch.int16, device=DEV)
+    full = full.view(torch.bfloat16)
+    rq.kv_rope_insert_full(padded(kv, pad, case), dev(pos), dev(cache), dev(slots), full)
+    torch.cuda.synchronize()
+    exp = oracle.kv_rope_quant_insert(kv, pos, cache, slots, np.full((nb, stride), 0xAA, np.uint8),
+                                      bs, stride, FMT[fmt])
+    got = host(k_cache)
+    rec = np.zeros(exp.size, bool)
+    for s in slots[slots >= 0]:
+        off = (s // bs) * stride + (s % bs) * 528
+        rec[off:off + 512] = True
+    rec = rec.reshape(exp.shape)
+    assert (got[~rec] == exp[~rec]).all(), "random kvi: bytes outside the codes differ"
+    assert_codes_match(got[rec], exp[rec], "random kvi codes")
+    ef = oracle.kv_rope_insert_full(kv, pos, cache, slots,
+                                    np.full((nb * bs, row), 0xAAAA, np.uint16))
+    assert_bits_equal(host(full), ef, "random kvf")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_indexer_random(case):
+    rng = np.random.default_rng([500, case])
+    N = int(rng.integers(1, 300))
+    H = int(rng.integers(1, 70))
+    thr = THREADS[case % 4]
+    hs = float(rng.uniform(0.25, 2.0))
+    print(f"[case] indexer random #{case}: N={N} H={H} threads={thr} head_scale={hs:.3f}",
+          flush=True)
+    rq.set_block_threads(thr)
+    q = synth.normal_bf16((N, H, 128), 510 + case, synth.T_Q, std=float(rng.uniform(0.01, 30)))
+    w = rng.uniform(0, 1, (N, H)).astype(np.float32)
+    pos = rng.integers(0, 65536, N).astype(np.int64)
+    cache = synth.cos_sin_cache(65536)
+    q8 = torch.empty((N, H, 128), dtype=torch.uint8, device=DEV)
+    wo = torch.empty((N, H), dtype=torch.float32, device=DEV)
+    rq.indexer_q_rope_quant(dev(q), dev(pos), dev(cache), dev(w), q8, wo, 128 ** -0.5, hs)
+    torch.cuda.synchronize()
+    ec, ew = oracle.indexer_q_rope_quant(q, pos, cache, w, 128 ** -0.5, hs)
+    assert_bits_equal(host(wo), ew, "random indexer weights")
+    assert_codes_match(host(q8), ec, "random indexer codes")
+
+
+def test_calls_run_in_order_on_the_callers_stream():
+    # Work is enqueued on the stream passed in: a long fill queued first on a
+    # side stream must finish before the op reads its input there, and the
+    # op's output must be complete when that stream is synchronized.
+    o, pos, cache = synth.irq_inputs(dict(synth.IRQ_TINY, N=64, H=16, hpg=8, seed=600))
+    od = dev(o)
+    scratch = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    src = torch.zeros_like(od)
+    out, sc = rq.empty_inv_rope_fp8_quant_outputs(64, 16, 8, DEV)
+    print("[case] stream ordering", flush=True)
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            scratch.fill_(3)  # slow work ahead of the copy
+        src.copy_(od)
+        rq.inv_rope_fp8_quant(src, dev(pos), dev(cache), 8, out, sc, stream=side)
+    side.synchronize()
+    eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, 8)
+    assert_bits_equal(host(sc), es, "side-stream scales")
+    assert_codes_match(host(out), eo, "side-stream codes")
