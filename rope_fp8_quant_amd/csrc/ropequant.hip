@@ -340,10 +340,12 @@ __device__ __forceinline__ void store_rows_bf16(uint4* lds_wave, const uint4 (&o
 // and the row reads free of bank conflicts.  Lanes 0..31 store units 0 and 2,
 // lanes 32..63 units 1 and 3 (constant indices throughout, so the base
 // pointers stay in scalar registers).  Unit k is stored when
-// unit0 + k < units (a tail wave past the last unit stores nothing).  NT:
-// nontemporal stores, faster for the q path's rows (half of them pad rows)
-// and slower for inv_rope_fp8_quant's, as measured.
-template <bool NT>
+// unit0 + k < units (a tail wave past the last unit stores nothing).  The
+// stores are nontemporal.  Timed with each launch on buffers the previous
+// launches have not touched, as in a model, they beat plain stores for both
+// inv_rope_fp8_quant (by 6%) and the q path (by 2%).  Relaunched on the same
+// output, plain stores win instead: they overwrite lines the last launch
+// left in the last-level cache.
 __device__ __forceinline__ void store_rows_fp8(uint4* lds_wave, const uint32_t (&codes)[8],
                                                int lane, uint8_t* const (&dst)[4],
                                                uint32_t unit0, uint32_t units) {
@@ -364,13 +366,8 @@ __device__ __forceinline__ void store_rows_fp8(uint4* lds_wave, const uint32_t (
   const uint4 c01 = *reinterpret_cast<const uint4*>(lds8 + 64 * half + (G0 ^ ((sw ^ half) << 2)));
   const uint4 c23 =
       *reinterpret_cast<const uint4*>(lds8 + 64 * (2 + half) + (G0 ^ ((sw ^ half) << 2)));
-  if (NT) {
-    if (unit0 + half < units) store_nt(base01 + 16 * j16, c01);
-    if (unit0 + 2 + half < units) store_nt(base23 + 16 * j16, c23);
-  } else {
-    if (unit0 + half < units) *reinterpret_cast<uint4*>(base01 + 16 * j16) = c01;
-    if (unit0 + 2 + half < units) *reinterpret_cast<uint4*>(base23 + 16 * j16) = c23;
-  }
+  if (unit0 + half < units) store_nt(base01 + 16 * j16, c01);
+  if (unit0 + 2 + half < units) store_nt(base23 + 16 * j16, c23);
 }
 
 // Launch shape, filled in by the host: every params struct starts with it.
@@ -491,10 +488,10 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     // scales.  A unit whose position is outside the table gets NaN scales,
     // which turns all of its dequantized values into NaN.  FP32 scales laid
     // out four to a head (the group-major and token-major layouts) are
-    // gathered into the row's first lane and written with one nontemporal
-    // 16-byte store: the per-block 4-byte stores of 16 lanes, through the
-    // cache, measured 3.5% slower over the whole kernel.  Other layouts
-    // (MN-major) take one 4-byte store per block.
+    // gathered into the row's first lane and written with one 16-byte
+    // store: the per-block 4-byte stores of 16 lanes measured 3.5% slower
+    // over the whole kernel, and a nontemporal 16-byte store 1% slower.
+    // Other layouts (MN-major) take one 4-byte store per block.
     if (unit0 + q < p.units) {
       const bool bad = PICK_ROW(q, badk) != 0;
       uint8_t* sc = PICK_ROW(q, sck);
@@ -509,14 +506,15 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
           const float s2 = dpp_f32<kRowShl8>(sv);
           const float s3 = dpp_f32<kRowShl12>(sv);
           if (L == 0)
-            store_nt(sc, make_uint4(__builtin_bit_cast(uint32_t, sv), __builtin_bit_cast(uint32_t, s1),
-                                    __builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, s3)));
+            *reinterpret_cast<uint4*>(sc) =
+                make_uint4(__builtin_bit_cast(uint32_t, sv), __builtin_bit_cast(uint32_t, s1),
+                           __builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, s3));
         } else if (r == 0) {
           reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = sv;
         }
       }
     }
-    store_rows_fp8<false>(lds_wave, codes, lane, outk, unit0, p.units);
+    store_rows_fp8(lds_wave, codes, lane, outk, unit0, p.units);
   }
 }
 
@@ -715,7 +713,7 @@ __device__ __forceinline__ void qnr_body(const QnrParams& p, uint32_t wave, uint
         static_cast<float*>(p.q_scales)[4 * u + blk] = poison ? __builtin_nanf("") : scale;
       }
     }
-    store_rows_fp8<true>(lds_wave, codes, lane, dst, unit0, p.units);
+    store_rows_fp8(lds_wave, codes, lane, dst, unit0, p.units);
   }
 }
 
@@ -1023,14 +1021,22 @@ Magic make_magic(uint32_t d) {
   return Magic{(uint32_t)m, 31u + s};
 }
 
+// Per-kernel launch shape, timed on MI355X: the XCD chunk size (log2
+// workgroups) and the workgroup size for many units.
+struct LaunchShape {
+  uint32_t chunk_log2;
+  int prefill_threads;
+};
+
 // Launch table: the analogue of [P4] section 4's program-count rule.  Many
-// units (prefill): 256-thread workgroups (16 units), plenty of them per CU.
-// Few units (decode): 64-thread workgroups (4 units) so the work spreads over
-// as many CUs as possible.  Results do not depend on the choice.
-int pick_block_threads(uint32_t units) {
+// units (prefill): the kernel's prefill workgroup size (128 or 256 threads,
+// 8 or 16 units), plenty of workgroups per CU.  Few units (decode): 64-thread
+// workgroups (4 units) so the work spreads over as many CUs as possible.
+// Results do not depend on the choice.
+int pick_block_threads(uint32_t units, int prefill_threads) {
   const int forced = g_block_threads.load(std::memory_order_relaxed);
   if (forced) return forced;
-  return units >= 16384u ? 256 : 64;
+  return units >= 16384u ? prefill_threads : 64;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -1064,12 +1070,12 @@ bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
 }
 
 // Every params struct starts with a LaunchHdr, filled in here.
-int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
+int launch(const void* fn, uint32_t units, LaunchShape shape, void* params,
            hipStream_t stream, bool uses_lds = true) {
-  const int threads = pick_block_threads(units);
+  const int threads = pick_block_threads(units, shape.prefill_threads);
   LaunchHdr* hdr = static_cast<LaunchHdr*>(params);
   hdr->wpb_log2 = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
-  hdr->chunk_log2 = chunk_log2;
+  hdr->chunk_log2 = shape.chunk_log2;
   const uint32_t per_block = (uint32_t)threads / 16u;
   const uint32_t blocks = (units + per_block - 1) / per_block;
   void* args[] = {params};
@@ -1079,11 +1085,14 @@ int launch(const void* fn, uint32_t units, uint32_t chunk_log2, void* params,
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
-// XCD chunk sizes (log2 workgroups), timed on MI355X per kernel.
-constexpr uint32_t kIrqChunkLog2 = 6;
-constexpr uint32_t kQnrChunkLog2 = 4;
-constexpr uint32_t kKviChunkLog2 = 4;
-constexpr uint32_t kIdxChunkLog2 = 4;
+// Timed with every launch on buffers that earlier launches have not touched.
+constexpr LaunchShape kIrqShape{6, 128};  // FP8 codes
+constexpr LaunchShape kIrbShape{6, 256};  // bf16 rows
+constexpr LaunchShape kQnrShape{4, 256};  // bf16 q_out
+constexpr LaunchShape kQf8Shape{4, 256};  // FP8 q_out
+constexpr LaunchShape kFusedShape{4, 256};
+constexpr LaunchShape kKviShape{4, 256};
+constexpr LaunchShape kIdxShape{4, 256};
 
 bool finite_f32(double v) {
   const float f = (float)v;
@@ -1159,7 +1168,7 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
               sc_stride_token % 4 == 0 && aligned(scales, 16);
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)irq_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.units, kIrqChunkLog2, &p, (hipStream_t)stream);
+  return launch(fn, p.units, kIrqShape, &p, (hipStream_t)stream);
 }
 
 int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
@@ -1197,7 +1206,7 @@ int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_he
   p.out = reinterpret_cast<uint8_t*>(out);
   p.out_sg = 2 * out_stride_group; p.out_st = 2 * out_stride_token;  // bytes in the kernel
   p.scales = nullptr; p.sc_sg = p.sc_st = p.sc_sb = 0; p.sc_vec4 = 0;
-  return launch((const void*)irq_kernel<kOutBf16>, p.units, kIrqChunkLog2, &p,
+  return launch((const void*)irq_kernel<kOutBf16>, p.units, kIrbShape, &p,
                 (hipStream_t)stream);
 }
 
@@ -1339,7 +1348,7 @@ const void* fused_fn(bool has_weight) {
 int launch_fused(const void* fn, FusedParams& p, void* stream) {
   p.q_waves = (p.q.units + 3u) / 4u;
   const uint32_t kv_waves = (p.k.n_tokens + 3u) / 4u;
-  return launch(fn, 4u * (p.q_waves + kv_waves), kQnrChunkLog2, &p, (hipStream_t)stream);
+  return launch(fn, 4u * (p.q_waves + kv_waves), kFusedShape, &p, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -1357,7 +1366,7 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
                           cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps,
                           kOutBf16, q_out, nullptr, nullptr, 0.0, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  return launch(qnr_fn<kOutBf16>(norm_weight != nullptr), p.units, kQnrChunkLog2, &p,
+  return launch(qnr_fn<kOutBf16>(norm_weight != nullptr), p.units, kQnrShape, &p,
                 (hipStream_t)stream);
 }
 
@@ -1376,7 +1385,7 @@ int qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
   const bool w = norm_weight != nullptr;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? qnr_fn<RQ_SCALE_UE8M0>(w)
                                                : qnr_fn<RQ_SCALE_FP32>(w);
-  return launch(fn, p.units, kQnrChunkLog2, &p, (hipStream_t)stream);
+  return launch(fn, p.units, kQf8Shape, &p, (hipStream_t)stream);
 }
 
 int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
@@ -1393,7 +1402,7 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
   if (rc != RQ_OK || empty) return rc;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)kvi_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.n_tokens, kKviChunkLog2, &p, (hipStream_t)stream);
+  return launch(fn, p.n_tokens, kKviShape, &p, (hipStream_t)stream);
 }
 
 int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
@@ -1405,7 +1414,7 @@ int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token, const int64
   const int rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping,
                           n_tokens, cache, num_slots, cache_stride_token, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  return launch((const void*)kvi_kernel<kOutBf16>, p.n_tokens, kKviChunkLog2, &p,
+  return launch((const void*)kvi_kernel<kOutBf16>, p.n_tokens, kKviShape, &p,
                 (hipStream_t)stream);
 }
 
@@ -1512,7 +1521,7 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
   p.wo = weights_out; p.wo_st = wo_stride_token;
   // 4 * kIdxRounds heads per wave: size the launch in rows of kIdxRounds heads
   const uint32_t rows = (p.units + kIdxRounds - 1) / kIdxRounds;
-  return launch((const void*)idx_kernel, rows, kIdxChunkLog2, &p, (hipStream_t)stream, false);
+  return launch((const void*)idx_kernel, rows, kIdxShape, &p, (hipStream_t)stream, false);
 }
 
 }  // extern "C"
