@@ -290,8 +290,9 @@ int qnorm_rope_fp8_kv_rope_insert_full(
  *   contiguous); weights_out may be weights itself (in place).  q_fp8: e4m3
  *   [N, H, 128] with byte strides (out_stride_token, out_stride_head), 8-byte
  *   aligned, multiples of 8, rows not overlapping.  softmax_scale, head_scale
- *   finite (as fp32); eps >= 2^-116 as fp32.  n_tokens * n_heads < 2^31.
- *   A head whose position is out of range gets a NaN weight.
+ *   finite (as fp32); eps >= 2^-116 as fp32.  n_tokens * n_heads < 2^31;
+ *   q_stride_head <= 2^28 and out_stride_head <= 2^30 (RQ_ERR_STRIDE
+ *   otherwise).  A head whose position is out of range gets a NaN weight.
  */
 int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,
                          const int64_t* positions, const float* cos_sin_cache, int64_t max_pos,
@@ -302,8 +303,9 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
 
 /*
  * Launch-shape knob (process-wide, thread-safe): 0 lets the launch table pick
- * the workgroup size from the unit count (256 threads for >= 16384 units,
- * else 64, the analogue of [P4] section 4's program-count rule); 64, 128 or
+ * the workgroup size from the unit count (for >= 16384 units 128 threads for
+ * inv_rope_fp8_quant and 256 for the other calls, else 64: the analogue of
+ * [P4] section 4's program-count rule); 64, 128 or
  * 256 forces that size for every later launch.  Results never depend on it;
  * it exists for tuning and for the launch-invariance tests.  Returns RQ_OK
  * or RQ_ERR_VALUE.

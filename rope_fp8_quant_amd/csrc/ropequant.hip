@@ -101,14 +101,27 @@ constexpr int kRowShl4 = 0x104;       // lane i <- lane i+4 within the row
 constexpr int kRowShl8 = 0x108;       // lane i <- lane i+8 within the row
 constexpr int kRowShl12 = 0x10C;      // lane i <- lane i+12 within the row
 
+// Every control used here either has a source lane for each lane or leaves
+// the lanes without one at 0, so bound_ctrl (write 0) and an old value of 0
+// agree; with bound_ctrl set the compiler needs no zeroed destination first.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// max(m, m of the lane CTRL names) for m >= 0 and not NaN, which every
+// per-lane block maximum of NaN-free inputs is: such floats order like their
+// bit patterns, and the integer max takes the DPP read as an operand where
+// a float max would first quiet it.
+template <int CTRL>
+__device__ __forceinline__ float max_dpp_nonneg(float m) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, m);
+  return __builtin_bit_cast(float, max(u, dpp_u32<CTRL>(u)));
 }
 
 // The lane's 32 values: x[k][e] is dim lane_dim0 + 32k + e.
@@ -247,8 +260,8 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
   for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v.x[k][e]));
-  m = __builtin_fmaxf(m, dpp_f32<kQuadSwap1>(m));
-  m = __builtin_fmaxf(m, dpp_f32<kQuadSwap2>(m));
+  m = max_dpp_nonneg<kQuadSwap1>(m);
+  m = max_dpp_nonneg<kQuadSwap2>(m);
   m = __builtin_fmaxf(m, eps);
   float mult;
   if (FMT == RQ_SCALE_UE8M0) {
@@ -875,10 +888,18 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
 // DPP row rotation by 8 brings each lane its partner's 4 values, and all 16
 // lanes rotate 4 values each (a layout with 8 consecutive dims per lane left
 // half the lanes idle through the rotation and took 31% more VALU
-// instructions; this one measured 5.7% faster).  A wave takes 4 * kIdxRounds
-// heads in kIdxRounds rounds, software-pipelined (below): 4.5% faster than
-// issuing all rounds' reads first.  More rounds per wave (3, 4, 8, pipelined
-// or not), late per-round loads and scalar positions were all slower.
+// instructions; this one measured 5.7% faster).
+//
+// Work is dealt in items of 4 consecutive heads of one token (a token's last
+// item may hold fewer).  The item's token, position, cos/sin row and base
+// addresses are then wave-uniform and live in scalar registers; each lane
+// only adds an offset fixed for the whole kernel.  (Per-lane 64-bit address
+// arithmetic had made the kernel issue-bound: 291 VALU instructions per
+// wave, 26 of them quarter-rate 64-bit multiplies; now 188.)  A wave takes
+// kIdxRounds items, its loads issued before the first item's arithmetic.
+// The weight is read where lane 0 folds it; the compiler sinks the first
+// item's weight load into that branch, which timed 4% faster than forcing
+// it up front and 12% faster than sinking both.
 struct IdxParams {
   LaunchHdr hdr;
   const uint16_t* q;
@@ -888,9 +909,9 @@ struct IdxParams {
   int64_t max_pos;
   const float* w;
   int64_t w_st;
-  uint32_t units;  // n_tokens * n_heads
-  Magic div_heads;
-  uint32_t n_heads;
+  uint32_t items;  // n_tokens * quads
+  Magic div_quads;
+  uint32_t quads, n_heads;  // quads = ceil(n_heads / 4)
   float softmax_scale, head_scale, eps;
   uint8_t* out;
   int64_t out_st, out_sh;
@@ -898,62 +919,65 @@ struct IdxParams {
   int64_t wo_st;
 };
 
-constexpr int kIdxRounds = 2;    // heads per row per wave (2 timed best of 1, 2, 3, 4, 8)
+constexpr int kIdxRounds = 2;    // items per wave (2 timed best of 1, 2, 3, 4, 8)
 
 constexpr int kRowRor8 = 0x128;  // lane i <- lane i^8 within the row (rotate by 8 of 16)
 
-__device__ __forceinline__ uint2 load_nt8(const uint16_t* p) {
+__device__ __forceinline__ uint2 load_nt8(const uint8_t* p) {
   typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t v = __builtin_nontemporal_load((__attribute__((address_space(1))) const u32x2_t*)p);
   return make_uint2(v.x, v.y);
 }
 
-// Software-pipelined: round j's rows and position are requested two rounds
-// ahead, its cos/sin and weight one round ahead; scheduling barriers keep the
-// compiler from hoisting every round's loads to the top.
 template <int ROUNDS>
-__device__ __forceinline__ void idx_pipelined(const IdxParams& p, uint32_t unit0, int lane) {
+__device__ __forceinline__ void idx_items(const IdxParams& p, uint32_t item0, int lane) {
   const int q = lane >> 4, L = lane & 15;
-  uint2 ra[3], rb[3];
-  int64_t pos[3];
-  uint32_t tj[3], hj[3];
-  float4 cv[2], sv[2];
-  float wg[2];
-  bool bad[2];
-  auto issue = [&](int j) {
-    const uint32_t u = min(unit0 + 4u * j + q, p.units - 1u);
-    const uint32_t t = magic_div(u, p.div_heads);
-    tj[j % 3] = t;
-    hj[j % 3] = u - t * p.n_heads;
-    pos[j % 3] = p.positions[t];
-    const uint16_t* row = p.q + (int64_t)t * p.q_st + (int64_t)hj[j % 3] * p.q_sh + 4 * L;
-    ra[j % 3] = load_nt8(row);
-    rb[j % 3] = load_nt8(row + 64);
-  };
-  auto fetch_cs = [&](int j) {
-    const int64_t ps = pos[j % 3];
-    const bool b = ps < 0 || ps >= p.max_pos;
-    bad[j % 2] = b;
-    const float4* row = reinterpret_cast<const float4*>(p.cs + (b ? 0 : ps) * 64);
-    cv[j % 2] = row[L & 7];
-    sv[j % 2] = row[8 + (L & 7)];
-    wg[j % 2] = p.w[(int64_t)tj[j % 3] * p.w_st + hj[j % 3]];
-  };
-  issue(0);
-  if (ROUNDS > 1) issue(1);
-  fetch_cs(0);
+  // Row q of an item is head 4g + q; the host keeps these offsets in 32 bits.
+  const uint32_t q_row_off = (uint32_t)q * (uint32_t)p.q_sh * 2u;
+  const uint32_t o_row_off = (uint32_t)q * (uint32_t)p.out_sh;
+  uint32_t tj[ROUNDS], h0j[ROUNDS], nvj[ROUNDS];
+  uint2 ra[ROUNDS], rb[ROUNDS];
+  // Item j's head rows.  A slot past the last item repeats the last item, and
+  // a row past the token's last head reads the item's first row: every read
+  // stays inside q, and neither stores anything.
 #pragma unroll
   for (int j = 0; j < ROUNDS; ++j) {
-    if (j + 1 < ROUNDS) fetch_cs(j + 1);
-    if (j + 2 < ROUNDS) issue(j + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    const int s3 = j % 3, s2 = j % 2;
-    const uint32_t par0 = dpp_u32<kRowRor8>(ra[s3].x);
-    const uint32_t par1 = dpp_u32<kRowRor8>(ra[s3].y);
-    const uint32_t pw[2] = {par0, par1}, ow[2] = {ra[s3].x, ra[s3].y};
-    const float c4[4] = {cv[s2].x, cv[s2].y, cv[s2].z, cv[s2].w};
-    const float s4[4] = {sv[s2].x, sv[s2].y, sv[s2].z, sv[s2].w};
-    const bool first = L < 8;
+    const uint32_t i = min(item0 + j, p.items - 1u);
+    const uint32_t t = magic_div(i, p.div_quads);
+    const uint32_t h0 = 4u * (i - t * p.quads);
+    tj[j] = t;
+    h0j[j] = h0;
+    nvj[j] = min(4u, p.n_heads - h0);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(p.q + (int64_t)t * p.q_st +
+                                                           (int64_t)h0 * p.q_sh);
+    const uint32_t off = ((uint32_t)q < nvj[j] ? q_row_off : 0u) + 8u * L;
+    ra[j] = load_nt8(base + off);
+    rb[j] = load_nt8(base + off + 128);
+  }
+  int64_t pos[ROUNDS];
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) pos[j] = load_uniform(p.positions + tj[j]);
+  float4 cv[ROUNDS], sv[ROUNDS];
+  float wg[ROUNDS];
+  bool bad[ROUNDS];
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) {
+    bad[j] = pos[j] < 0 || pos[j] >= p.max_pos;
+    const float4* row = reinterpret_cast<const float4*>(p.cs + (bad[j] ? 0 : pos[j]) * 64);
+    cv[j] = row[L & 7];
+    sv[j] = row[8 + (L & 7)];
+    const float* wrow = p.w + (int64_t)tj[j] * p.w_st + h0j[j];
+    wg[j] = wrow[(uint32_t)q < nvj[j] ? q : 0];
+  }
+  // Lanes 0..7 hold dims i < 32 and subtract their partner's term: flipping
+  // the partner's sign bits is exact and gives the same products.
+  const uint32_t flip = L < 8 ? 0x80008000u : 0u;
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) {
+    const uint32_t pw[2] = {dpp_u32<kRowRor8>(ra[j].x) ^ flip, dpp_u32<kRowRor8>(ra[j].y) ^ flip};
+    const uint32_t ow[2] = {ra[j].x, ra[j].y};
+    const float c4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+    const float s4[4] = {sv[j].x, sv[j].y, sv[j].z, sv[j].w};
     float x[8];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -962,22 +986,21 @@ __device__ __forceinline__ void idx_pipelined(const IdxParams& p, uint32_t unit0
         const int e = 2 * i + h;
         const float own = h ? bf_hi(ow[i]) : bf_lo(ow[i]);
         const float prt = h ? bf_hi(pw[i]) : bf_lo(pw[i]);
-        const float sg = first ? -s4[e] : s4[e];
-        const float y = own * c4[e] + prt * sg;
+        const float y = own * c4[e] + prt * s4[e];
         x[e] = (float)(__bf16)y;
       }
     }
-    x[4] = bf_lo(rb[s3].x);
-    x[5] = bf_hi(rb[s3].x);
-    x[6] = bf_lo(rb[s3].y);
-    x[7] = bf_hi(rb[s3].y);
+    x[4] = bf_lo(rb[j].x);
+    x[5] = bf_hi(rb[j].x);
+    x[6] = bf_lo(rb[j].y);
+    x[7] = bf_hi(rb[j].y);
     float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
-    m = __builtin_fmaxf(m, dpp_f32<kQuadSwap1>(m));
-    m = __builtin_fmaxf(m, dpp_f32<kQuadSwap2>(m));
-    m = __builtin_fmaxf(m, dpp_f32<kRowHalfMirror>(m));
-    m = __builtin_fmaxf(m, dpp_f32<kRowMirror>(m));
+    m = max_dpp_nonneg<kQuadSwap1>(m);
+    m = max_dpp_nonneg<kQuadSwap2>(m);
+    m = max_dpp_nonneg<kRowHalfMirror>(m);
+    m = max_dpp_nonneg<kRowMirror>(m);
     m = __builtin_fmaxf(m, p.eps);
     const uint32_t tb = __builtin_bit_cast(uint32_t, m < __builtin_inff() ? div448(m) : m);
     const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
@@ -992,22 +1015,22 @@ __device__ __forceinline__ void idx_pipelined(const IdxParams& p, uint32_t unit0
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, wd, true);
       code[h] = (uint32_t)wd;
     }
-    if (unit0 + 4u * j + q < p.units) {
-      uint8_t* orow = p.out + (int64_t)tj[s3] * p.out_st + (int64_t)hj[s3] * p.out_sh;
-      __builtin_nontemporal_store(code[0], (__attribute__((address_space(1))) uint32_t*)(orow + 4 * L));
-      __builtin_nontemporal_store(code[1], (__attribute__((address_space(1))) uint32_t*)(orow + 64 + 4 * L));
+    if (item0 + j < p.items && (uint32_t)q < nvj[j]) {
+      uint8_t* orow = p.out + (int64_t)tj[j] * p.out_st + (int64_t)h0j[j] * p.out_sh;
+      const uint32_t off = o_row_off + 4u * L;
+      __builtin_nontemporal_store(code[0], (__attribute__((address_space(1))) uint32_t*)(orow + off));
+      __builtin_nontemporal_store(code[1], (__attribute__((address_space(1))) uint32_t*)(orow + off + 64));
       if (L == 0) {
-        const float fold = ((wg[s2] * qs) * p.softmax_scale) * p.head_scale;
-        p.wo[(int64_t)tj[s3] * p.wo_st + hj[s3]] = bad[s2] ? __builtin_nanf("") : fold;
+        const float fold = ((wg[j] * qs) * p.softmax_scale) * p.head_scale;
+        p.wo[(int64_t)tj[j] * p.wo_st + h0j[j] + q] = bad[j] ? __builtin_nanf("") : fold;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
   const int lane = threadIdx.x & 63;
-  idx_pipelined<kIdxRounds>(p, wave_index(p.hdr) * (4u * kIdxRounds), lane);
+  idx_items<kIdxRounds>(p, wave_index(p.hdr) * kIdxRounds, lane);
 }
 
 // ------------------------------------------------------------ host side
@@ -1510,17 +1533,21 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
     const int64_t sw[2] = {wo_stride_token, 1};
     if (!no_overlap(2, n, sw, 1)) return RQ_ERR_STRIDE;
   }
+  // per-lane offsets inside a 4-head item are kept in 32 bits
+  if (q_stride_head > (int64_t(1) << 28) || out_stride_head > (int64_t(1) << 30))
+    return RQ_ERR_STRIDE;
   IdxParams p;
   p.q = q; p.q_st = q_stride_token; p.q_sh = q_stride_head;
   p.positions = positions; p.cs = cos_sin_cache; p.max_pos = max_pos;
   p.w = weights; p.w_st = w_stride_token;
-  p.units = (uint32_t)(n_tokens * n_heads);
-  p.div_heads = make_magic((uint32_t)n_heads); p.n_heads = (uint32_t)n_heads;
+  p.quads = (uint32_t)((n_heads + 3) / 4);
+  p.items = (uint32_t)(n_tokens * p.quads);
+  p.div_quads = make_magic(p.quads); p.n_heads = (uint32_t)n_heads;
   p.softmax_scale = (float)softmax_scale; p.head_scale = (float)head_scale; p.eps = (float)eps;
   p.out = q_fp8; p.out_st = out_stride_token; p.out_sh = out_stride_head;
   p.wo = weights_out; p.wo_st = wo_stride_token;
-  // 4 * kIdxRounds heads per wave: size the launch in rows of kIdxRounds heads
-  const uint32_t rows = (p.units + kIdxRounds - 1) / kIdxRounds;
+  // kIdxRounds items per wave; `launch` sizes grids in 16-lane rows, 4 per wave
+  const uint32_t rows = 4u * ((p.items + kIdxRounds - 1) / kIdxRounds);
   return launch((const void*)idx_kernel, rows, kIdxShape, &p, (hipStream_t)stream, false);
 }
 

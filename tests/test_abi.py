@@ -206,6 +206,8 @@ def test_indexer_zero_tokens_is_ok_without_pointers():
     (dict(ss=1e300), VALUE),
     (dict(q=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL), (dict(wo=None), NULL),
     (dict(qst=0), STRIDE), (dict(wost=0), STRIDE), (dict(osh=64), STRIDE), (dict(wost=32), STRIDE),
+    # per-lane offsets inside a 4-head item must fit in 32 bits
+    (dict(qsh=(1 << 28) + 8), STRIDE), (dict(osh=(1 << 30) + 8), STRIDE),
     (dict(q=A + 8), ALIGN), (dict(qsh=132), ALIGN), (dict(out=A + 4), ALIGN),
     (dict(osh=132), ALIGN), (dict(w=A + 2), ALIGN), (dict(cs=A + 4), ALIGN),
 ])
