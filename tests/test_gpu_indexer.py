@@ -75,6 +75,30 @@ def test_indexer_strided_input_and_in_place_weights():
     assert_codes_match(got, exp, "strided codes")
 
 
+@pytest.mark.parametrize("threads", [64, 256])
+def test_indexer_strided_outputs_partial_item(threads):
+    # 7 heads: every token's second 4-head item holds 3 heads.  Codes rows
+    # padded to 192 bytes, weight rows to 10 and 12 floats; the padding must
+    # come back untouched.
+    rq.set_block_threads(threads)
+    N, H = 41, 7
+    q, w, pos, cache = idx_inputs(N, H, 62, max_pos=65536)
+    q8_big = torch.full((N, H, 192), 0xCD, dtype=torch.uint8, device=DEV)
+    w_big = torch.full((N, 10), -7.0, dtype=torch.float32, device=DEV)
+    w_big[:, :H] = dev(w)
+    wo_big = torch.full((N, 12), -3.0, dtype=torch.float32, device=DEV)
+    print(f"[case] indexer strided outputs threads={threads}", flush=True)
+    rq.indexer_q_rope_quant(dev(q), dev(pos), dev(cache), w_big[:, :H], q8_big[:, :, :128],
+                            wo_big[:, :H], SOFTMAX_SCALE, 0.5)
+    torch.cuda.synchronize()
+    exp, ew = oracle.indexer_q_rope_quant(q, pos, cache, w, SOFTMAX_SCALE, 0.5)
+    g8, gw = host(q8_big), host(wo_big)
+    assert_bits_equal(gw[:, :H], ew, "strided weights")
+    assert_codes_match(g8[:, :, :128], exp, "strided codes")
+    assert (g8[:, :, 128:] == 0xCD).all() and (gw[:, H:] == -3.0).all()
+    assert (host(w_big)[:, H:] == -7.0).all()
+
+
 def test_indexer_degenerate_heads():
     rng = np.random.default_rng(58)
     q = np.zeros((4, 8, 128), np.uint16)
