@@ -7,7 +7,10 @@ A step is one launch of ``inv_rope_fp8_quant`` over the prefill workload
 (16384 tokens x 32 heads in 4 groups of 8, head dim 512, bf16 in, e4m3 +
 fp32 block-128 scales out; synthetic inputs already resident in HBM).  The
 timed region is K back-to-back launches on one stream, bracketed by HIP
-events recorded on that same stream and by device synchronizations.  The JSON
+events recorded on that same stream and by device synchronizations.  Launch
+i works on buffer set i mod S, each set its own copy of the input and its own
+outputs, with S >= 2 and S sets totalling >= 1 GiB, so that no launch finds
+the lines it writes still in the last-level cache.  The JSON
 line reports achieved HBM throughput over the algorithmic bytes, tokens/s,
 the roofline fraction against the 8 TB/s HBM3E peak, HBM traffic from
 rocprofv3 counters when they were taken on the current kernel source, and
@@ -107,13 +110,13 @@ def time_launches(fn, steps, warmup, stream):
 
 
 # MI355X's MALL (last-level cache) holds 256 MB, and written lines stay in
-# it: relaunching on the same buffers lets a launch overwrite lines the last
-# one left there, which measured up to 16% faster for inv_rope_fp8_quant at
-# 818 MB per launch (and up to 15% for smaller configs) than any launch that
-# finds cold buffers.  In a model the next call on a buffer comes a layer
-# later, after other traffic has flushed the cache, so every config is timed
-# cycling through at least two copies of its buffers, and through enough
-# copies that they total ROTATE_BYTES.
+# it: relaunching on the same buffers lets plain stores overwrite lines the
+# last launch left there, which made an inv_rope_fp8_quant with plain code
+# stores 16% faster than with cold buffers (the nontemporal stores used now
+# gain about 1%).  In a model the next call on a buffer comes a layer later,
+# after other traffic has flushed the cache, so every config is timed cycling
+# through at least two copies of its buffers, and through enough copies that
+# they total ROTATE_BYTES.
 ROTATE_BYTES = 1 << 30
 
 
