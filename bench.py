@@ -419,25 +419,51 @@ def bench_copy(args, device, stream):
     return dict(bytes_read=n, bytes_written=n, us=ms * 1e3, gbs=2 * n / ms / 1e6)
 
 
-def cpu_baseline(irq_inputs, budget_s=12.0):
-    """The CPU oracle (single-threaded C) on this host, on a token prefix of
-    the prefill workload sized to about budget_s seconds of work."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(irq_inputs, budget_s=4.0, runs=3):
+    """The CPU oracle (single-threaded C) on this host, pinned to one core:
+    the median of `runs` runs over a token prefix of the prefill workload
+    sized to about budget_s seconds each (the whole workload if it fits)."""
     import oracle
     o, pos, cache = irq_inputs
     N, H = o.shape[0], o.shape[1]
-    n = 256
-    t = time.perf_counter()
-    oracle.inv_rope_fp8_quant(o[:n], pos[:n], cache, 8)
-    dt = time.perf_counter() - t
-    n2 = int(min(N, max(n, n * budget_s / max(dt, 1e-6))))
-    t = time.perf_counter()
-    oracle.inv_rope_fp8_quant(np.ascontiguousarray(o[:n2]), pos[:n2].copy(), cache, 8)
-    dt = time.perf_counter() - t
+    try:
+        old_aff = os.sched_getaffinity(0)
+        core = min(old_aff)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        old_aff, core = None, None
+    try:
+        n = 256
+        t = time.perf_counter()
+        oracle.inv_rope_fp8_quant(o[:n], pos[:n], cache, 8)
+        dt = time.perf_counter() - t
+        n2 = int(min(N, max(n, n * budget_s / max(dt, 1e-6))))
+        oc, pc = np.ascontiguousarray(o[:n2]), pos[:n2].copy()
+        times = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            oracle.inv_rope_fp8_quant(oc, pc, cache, 8)
+            times.append(time.perf_counter() - t)
+    finally:
+        if old_aff is not None:
+            os.sched_setaffinity(0, old_aff)
+    dt = sorted(times)[len(times) // 2]
     gbs = irq_bytes(n2, H) / dt / 1e9
     return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
-                tokens_per_s=round(n2 / dt, 1),
+                tokens_per_s=round(n2 / dt, 1), cpu=cpu_model(),
                 sample=f"first {n2} of {N} tokens x {H} heads of the same workload, one "
-                       f"thread, {dt:.1f} s")
+                       f"thread pinned to core {core}, median of {runs} runs of {dt:.1f} s")
 
 
 def _oracle_shard_proc(spec, results):
@@ -499,7 +525,15 @@ def cpu_baseline_sharded(irq_inputs):
         procs = [ctx.Process(target=_oracle_shard_proc, args=(sp, results)) for sp in specs]
         for pr in procs:
             pr.start()
-        times = [results.get() for _ in procs]
+        times = []
+        while len(times) < len(procs):
+            if not results.empty():
+                times.append(results.get())
+            elif not any(pr.is_alive() for pr in procs) and results.empty():
+                # a worker died before reporting (e.g. it could not start)
+                times.append("a worker exited without a result")
+            else:
+                time.sleep(0.02)
         for pr in procs:
             pr.join()
         bad = [t for t in times if not isinstance(t, float)]
@@ -512,7 +546,7 @@ def cpu_baseline_sharded(irq_inputs):
         sc.unlink()
     dt = max(times)
     return dict(value=round(irq_bytes(N, H) / dt / 1e9, 4), unit="GB/s", cores=workers,
-                kind="oracle", tokens_per_s=round(N / dt, 1),
+                kind="oracle", tokens_per_s=round(N / dt, 1), cpu=cpu_model(),
                 sample=f"all {N} tokens x {H} heads split over {workers} processes, "
                        f"slowest shard {dt:.2f} s")
 
