@@ -629,7 +629,7 @@ def main():
         progress("decode")
         extra["decode"] = bench_decode(args, device, stream)
     line = {
-        "metric": "achieved HBM GB/s (% of peak) + tokens/s, inv_rope_fp8_quant 16k tok x 32 heads",
+        "metric": "achieved HBM GB/s (% of peak) + tokens/s, inv_rope_fp8_quant 16k tok\u00d732 heads",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -48,3 +48,22 @@ def test_bench_algorithmic_bytes_extend_the_pages_convention():
     # + 16 B of fp32 scales per head, 8 B position and a 256 B cos/sin row per token
     assert bench.irq_bytes(N, H) == pages_bytes + N * H * 16 + N * (8 + 256) == 818020352
     assert bench.irq_bytes(N, H, "ue8m0") == pages_bytes + N * H * 4 + N * 264
+
+
+def test_rotation_keeps_every_config_off_the_cache():
+    # at least two buffer sets, and together at least 1 GiB: 4x the 256 MB MALL
+    assert bench.rotation_sets(bench.irq_bytes(16384, 32)) == 2
+    assert bench.rotation_sets(bench.irq_bytes(4096, 48)) == 4
+    for b in (1, 4096, 14942208, 103841792, 306216960, 818020352, 1612776448):
+        s = bench.rotation_sets(b)
+        assert s >= 2 and s * b >= bench.ROTATE_BYTES
+        assert s == 2 or (s - 1) * b < bench.ROTATE_BYTES  # no more sets than needed
+
+
+def test_metric_names_the_headline_workload():
+    import json
+    import re
+    src = open(bench.__file__).read()
+    metric = json.loads(re.search(r'"metric": ("[^"]*")', src).group(1))
+    assert metric == ("achieved HBM GB/s (% of peak) + tokens/s, "
+                      "inv_rope_fp8_quant 16k tok×32 heads")
