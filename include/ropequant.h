@@ -49,6 +49,9 @@
  *     NaN (0x7FC0); and a slot outside [0, num_blocks * cache_block_size) is
  *     skipped.
  *   - Strides are in elements of the tensor's own type unless "bytes" is said.
+ *     Strides that place any element of a tensor more than 2^56 bytes from
+ *     its base (or overflow 64-bit arithmetic on the way) return
+ *     RQ_ERR_STRIDE: no device address space is that large.
  *   - Arithmetic: every fp32 step is an IEEE-754 basic operation rounded to
  *     nearest even, with no fused multiply-add; division and square root are
  *     correctly rounded; denormals are kept.

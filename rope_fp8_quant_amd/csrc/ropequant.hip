@@ -1087,9 +1087,28 @@ bool no_overlap(int nd, const int64_t* n, const int64_t* s, int64_t row) {
   int64_t span = row;  // elements covered by the inner dims so far
   for (int i = 0; i < m; ++i) {
     if (ss[i] < span) return false;
-    span = (ns[i] - 1) * ss[i] + span;
+    int64_t t;
+    if (__builtin_mul_overflow(ns[i] - 1, ss[i], &t) || __builtin_add_overflow(t, span, &span))
+      return false;
   }
   return true;
+}
+
+// A tensor of `nd` dims (extent n[i], stride s[i] >= 1, in elements of `elem`
+// bytes) over rows of `row` contiguous elements stays within 2^56 bytes of
+// its base, computed without overflow.  No device address space is that
+// large, so strides that fail this cannot describe a real tensor (and would
+// wrap the kernels' 64-bit address arithmetic).
+bool extent_ok(int nd, const int64_t* n, const int64_t* s, int64_t row, int64_t elem) {
+  int64_t last = row;
+  for (int i = 0; i < nd; ++i) {
+    if (n[i] <= 1) continue;
+    int64_t t;
+    if (__builtin_mul_overflow(n[i] - 1, s[i], &t) || __builtin_add_overflow(t, last, &last))
+      return false;
+  }
+  int64_t bytes;
+  return !__builtin_mul_overflow(last, elem, &bytes) && bytes <= (int64_t(1) << 56);
 }
 
 // Every params struct starts with a LaunchHdr, filled in here.
@@ -1169,13 +1188,18 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
     return RQ_ERR_ALIGN;
   const int64_t G = n_heads / heads_per_group;
   {
+    const int64_t n[2] = {n_tokens, n_heads}, s[2] = {o_stride_token, o_stride_head};
+    if (!extent_ok(2, n, s, kHeadDim, 2)) return RQ_ERR_STRIDE;
+  }
+  {
     const int64_t n[2] = {G, n_tokens}, s[2] = {out_stride_group, out_stride_token};
-    if (!no_overlap(2, n, s, (int64_t)heads_per_group * kHeadDim)) return RQ_ERR_STRIDE;
+    const int64_t row = (int64_t)heads_per_group * kHeadDim;
+    if (!no_overlap(2, n, s, row) || !extent_ok(2, n, s, row, 1)) return RQ_ERR_STRIDE;
   }
   {
     const int64_t per = scale_fmt == RQ_SCALE_FP32 ? (int64_t)heads_per_group * 4 : heads_per_group;
     const int64_t n[3] = {G, n_tokens, per}, s[3] = {sc_stride_group, sc_stride_token, sc_stride_block};
-    if (!no_overlap(3, n, s, 1)) return RQ_ERR_STRIDE;
+    if (!no_overlap(3, n, s, 1) || !extent_ok(3, n, s, 1, 4)) return RQ_ERR_STRIDE;
   }
   IrqParams p;
   p.o = o; p.o_st = o_stride_token; p.o_sh = o_stride_head;
@@ -1211,8 +1235,13 @@ int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_he
     return RQ_ERR_ALIGN;
   const int64_t G = n_heads / heads_per_group;
   {
+    const int64_t n[2] = {n_tokens, n_heads}, s[2] = {o_stride_token, o_stride_head};
+    if (!extent_ok(2, n, s, kHeadDim, 2)) return RQ_ERR_STRIDE;
+  }
+  {
     const int64_t n[2] = {G, n_tokens}, s[2] = {out_stride_group, out_stride_token};
-    if (!no_overlap(2, n, s, (int64_t)heads_per_group * kHeadDim)) return RQ_ERR_STRIDE;
+    const int64_t row = (int64_t)heads_per_group * kHeadDim;
+    if (!no_overlap(2, n, s, row) || !extent_ok(2, n, s, row, 2)) return RQ_ERR_STRIDE;
   }
   // in place only when every head's output lands on its own input row
   if (out == o && !(o_stride_head == kHeadDim && out_stride_token == o_stride_token &&
@@ -1256,6 +1285,10 @@ int prep_qnr(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head
   if (!q_in || !positions || !cos_sin_cache) return RQ_ERR_NULL;
   if (bf16 ? !q_out : (!q_fp8 || !q_scales)) return RQ_ERR_NULL;
   if (q_stride_token < 1 || q_stride_head < 1) return RQ_ERR_STRIDE;
+  {
+    const int64_t n[2] = {n_tokens, n_heads_q}, s[2] = {q_stride_token, q_stride_head};
+    if (!extent_ok(2, n, s, kHeadDim, 2)) return RQ_ERR_STRIDE;
+  }
   if (!aligned(q_in, 16) || (q_stride_token % 8) || (q_stride_head % 8) ||
       !aligned(positions, 8) || !aligned(cos_sin_cache, 16) ||
       (norm_weight && !aligned(norm_weight, 16)))
@@ -1313,6 +1346,9 @@ int prep_kvi(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positio
   if (n_tokens == 0) return RQ_OK;
   if (!kv || !positions || !cos_sin_cache || !slot_mapping || !k_cache) return RQ_ERR_NULL;
   if (kv_stride_token < 1) return RQ_ERR_STRIDE;
+  if (!extent_ok(1, &n_tokens, &kv_stride_token, kHeadDim, 2) ||
+      !extent_ok(1, &num_blocks, &block_stride_bytes, (int64_t)cache_block_size * kRecordBytes, 1))
+    return RQ_ERR_STRIDE;
   if (!aligned(kv, 16) || (kv_stride_token % 8) || !aligned(positions, 8) ||
       !aligned(cos_sin_cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
       (block_stride_bytes % 16))
@@ -1340,6 +1376,9 @@ int prep_kvf(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positio
   if (n_tokens == 0) return RQ_OK;
   if (!kv || !positions || !cos_sin_cache || !slot_mapping || !cache) return RQ_ERR_NULL;
   if (kv_stride_token < 1) return RQ_ERR_STRIDE;
+  if (!extent_ok(1, &n_tokens, &kv_stride_token, kHeadDim, 2) ||
+      !extent_ok(1, &num_slots, &cache_stride_token, kHeadDim, 2))
+    return RQ_ERR_STRIDE;
   if (!aligned(kv, 16) || (kv_stride_token % 8) || !aligned(positions, 8) ||
       !aligned(cos_sin_cache, 16) || !aligned(slot_mapping, 8) || !aligned(cache, 16) ||
       (cache_stride_token % 8))
@@ -1529,9 +1568,13 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
     return RQ_ERR_ALIGN;
   {
     const int64_t n[2] = {n_tokens, n_heads}, st[2] = {out_stride_token, out_stride_head};
-    if (!no_overlap(2, n, st, 128)) return RQ_ERR_STRIDE;
+    if (!no_overlap(2, n, st, 128) || !extent_ok(2, n, st, 128, 1)) return RQ_ERR_STRIDE;
     const int64_t sw[2] = {wo_stride_token, 1};
-    if (!no_overlap(2, n, sw, 1)) return RQ_ERR_STRIDE;
+    if (!no_overlap(2, n, sw, 1) || !extent_ok(1, &n_tokens, &wo_stride_token, n_heads, 4))
+      return RQ_ERR_STRIDE;
+    const int64_t sq[2] = {q_stride_token, q_stride_head};
+    if (!extent_ok(2, n, sq, 128, 2) || !extent_ok(1, &n_tokens, &w_stride_token, n_heads, 4))
+      return RQ_ERR_STRIDE;
   }
   // per-lane offsets inside a 4-head item are kept in 32 bits
   if (q_stride_head > (int64_t(1) << 28) || out_stride_head > (int64_t(1) << 30))

@@ -349,3 +349,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+@host_only
+@pytest.mark.parametrize("call,kw", [
+    (irq, dict(ost=1 << 56)), (irq, dict(osh=1 << 56)), (irq, dict(osg=1 << 60)),
+    (irq, dict(ost2=1 << 59)), (irq, dict(ssg=1 << 62)), (irq, dict(ssb=1 << 61)),
+    (irb, dict(ost=1 << 56)), (irb, dict(osg=1 << 60)),
+    (qnr, dict(qst=1 << 58)), (qnr, dict(qsh=1 << 55)),
+    (qf8, dict(qst=1 << 58)),
+    (kvi, dict(kst=1 << 58)), (kvi, dict(stride=1 << 60)),
+    (kvf, dict(kst=1 << 58)),
+    (idx, dict(qst=1 << 58)), (idx, dict(wst=1 << 62)), (idx, dict(ost=1 << 60)),
+    (idx, dict(wost=1 << 61)),
+], ids=lambda v: getattr(v, "__name__", None) or str(v))
+def test_strides_beyond_any_address_space_are_rejected(call, kw):
+    # a tensor whose strides reach past 2^56 bytes (or overflow int64 on the
+    # way) cannot exist; without this the kernels' address arithmetic wraps
+    assert call(**kw) == STRIDE
