@@ -54,9 +54,21 @@ def _same_device(ref, *named):
             raise ValueError(f"{name} must be on {ref.device}")
 
 
-def _stream(device, stream):
+def _call(name, device, stream, *args):
+    """Launch C entry point `name` on `stream` (default: torch's current stream
+    of `device`), with `device` current during the call, and raise on a
+    non-OK status.  The library launches on the current HIP device, so a
+    stream or tensors on another device would hand it foreign pointers."""
     s = torch.cuda.current_stream(device) if stream is None else stream
-    return s.cuda_stream
+    if s.device != device:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
+    fn = getattr(lib(), name)
+    if device.index is not None and device.index != torch.cuda.current_device():
+        with torch.cuda.device(device):
+            rc = fn(*args, s.cuda_stream)
+    else:
+        rc = fn(*args, s.cuda_stream)
+    check(name, rc)
 
 
 def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
@@ -134,13 +146,11 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
         raise ValueError(f"fp32 scales must be float32 [{G}, {N}, {hpg * 4}]")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"),
                  (scales, "scales"))
-    rc = lib().inv_rope_fp8_quant(
+    _call("inv_rope_fp8_quant", o.device, stream,
         o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], N, H, hpg, fmt, float(eps),
         out.data_ptr(), out.stride(0), out.stride(1),
-        scales.data_ptr(), scales.stride(0), scales.stride(1), scales.stride(2),
-        _stream(o.device, stream))
-    check("inv_rope_fp8_quant", rc)
+        scales.data_ptr(), scales.stride(0), scales.stride(1), scales.stride(2))
 
 
 def _check_o(o, heads_per_group):
@@ -166,11 +176,9 @@ def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None
             out.stride(2) != 1):
         raise ValueError(f"out must be bf16 [{G}, {N}, {hpg * 512}], last dim contiguous")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"))
-    rc = lib().inv_rope_bf16(
+    _call("inv_rope_bf16", o.device, stream,
         o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
-        cos_sin_cache.shape[0], N, H, hpg, out.data_ptr(), out.stride(0), out.stride(1),
-        _stream(o.device, stream))
-    check("inv_rope_bf16", rc)
+        cos_sin_cache.shape[0], N, H, hpg, out.data_ptr(), out.stride(0), out.stride(1))
 
 
 def _check_q_in(q_in, norm_weight, positions, cos_sin_cache):
@@ -259,12 +267,11 @@ def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, str
     norm_weight: bf16 [512] or None.  With q_head_padded == Hq, q_out may be
     q_in itself (contiguous): each head is read before it is written."""
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
-    rc = lib().qnorm_rope(
+    _call("qnorm_rope", q_in.device, stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
         cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, q_out.shape[1], float(eps),
-        q_out.data_ptr(), _stream(q_in.device, stream))
-    check("qnorm_rope", rc)
+        q_out.data_ptr())
 
 
 def qnorm_rope_fp8(q_in, norm_weight, positions, cos_sin_cache, q_fp8, q_scales, eps=1e-6,
@@ -275,12 +282,11 @@ def qnorm_rope_fp8(q_in, norm_weight, positions, cos_sin_cache, q_fp8, q_scales,
     fmt = _fmt(scale_fmt)
     N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
-    rc = lib().qnorm_rope_fp8(
+    _call("qnorm_rope_fp8", q_in.device, stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
         cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, hpad, float(eps), fmt,
-        float(quant_eps), q_fp8.data_ptr(), q_scales.data_ptr(), _stream(q_in.device, stream))
-    check("qnorm_rope_fp8", rc)
+        float(quant_eps), q_fp8.data_ptr(), q_scales.data_ptr())
 
 
 def kv_rope_insert_full(kv, positions, cos_sin_cache, slot_mapping, cache, stream=None):
@@ -288,11 +294,10 @@ def kv_rope_insert_full(kv, positions, cos_sin_cache, slot_mapping, cache, strea
     [num_slots, >= 512]: token t's row goes to cache[slot_mapping[t], :512]
     (skipped for a negative slot)."""
     N = _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache)
-    rc = lib().kv_rope_insert_full(
+    _call("kv_rope_insert_full", kv.device, stream,
         kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, cache.data_ptr(), cache.shape[0],
-        cache.stride(0), _stream(kv.device, stream))
-    check("kv_rope_insert_full", rc)
+        cache.stride(0))
 
 
 def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size,
@@ -302,11 +307,10 @@ def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, ca
     k_cache [num_blocks, block_bytes] (block stride = k_cache.stride(0))."""
     fmt = _fmt(scale_fmt)
     N = _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size)
-    rc = lib().kv_rope_quant_insert(
+    _call("kv_rope_quant_insert", kv.device, stream,
         kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, k_cache.data_ptr(), k_cache.shape[0],
-        k_cache.stride(0), int(cache_block_size), fmt, float(eps), _stream(kv.device, stream))
-    check("kv_rope_quant_insert", rc)
+        k_cache.stride(0), int(cache_block_size), fmt, float(eps))
 
 
 def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_cache,
@@ -317,14 +321,13 @@ def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_ca
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
     if _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    rc = lib().qnorm_rope_kv_rope_quant_insert(
+    _call("qnorm_rope_kv_rope_quant_insert", q_in.device, stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
         slot_mapping.data_ptr(), N, Hq, q_out.shape[1], float(eps), q_out.data_ptr(),
         k_cache.data_ptr(), k_cache.shape[0], k_cache.stride(0), int(cache_block_size), fmt,
-        float(quant_eps), _stream(q_in.device, stream))
-    check("qnorm_rope_kv_rope_quant_insert", rc)
+        float(quant_eps))
 
 
 def qnorm_rope_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cache,
@@ -334,13 +337,12 @@ def qnorm_rope_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cac
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    rc = lib().qnorm_rope_kv_rope_insert_full(
+    _call("qnorm_rope_kv_rope_insert_full", q_in.device, stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
         slot_mapping.data_ptr(), N, Hq, q_out.shape[1], float(eps), q_out.data_ptr(),
-        cache.data_ptr(), cache.shape[0], cache.stride(0), _stream(q_in.device, stream))
-    check("qnorm_rope_kv_rope_insert_full", rc)
+        cache.data_ptr(), cache.shape[0], cache.stride(0))
 
 
 def qnorm_rope_fp8_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cache,
@@ -353,14 +355,12 @@ def qnorm_rope_fp8_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    rc = lib().qnorm_rope_fp8_kv_rope_insert_full(
+    _call("qnorm_rope_fp8_kv_rope_insert_full", q_in.device, stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
         slot_mapping.data_ptr(), N, Hq, hpad, float(eps), fmt, float(quant_eps),
-        q_fp8.data_ptr(), q_scales.data_ptr(), cache.data_ptr(), cache.shape[0], cache.stride(0),
-        _stream(q_in.device, stream))
-    check("qnorm_rope_fp8_kv_rope_insert_full", rc)
+        q_fp8.data_ptr(), q_scales.data_ptr(), cache.data_ptr(), cache.shape[0], cache.stride(0))
 
 
 def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_out,
@@ -384,9 +384,8 @@ def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_ou
         raise ValueError("q_fp8 must be uint8/float8_e4m3fn [N, H, 128], last dim contiguous")
     _same_device(q, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
                  (weights, "weights"), (q_fp8, "q_fp8"), (weights_out, "weights_out"))
-    rc = lib().indexer_q_rope_quant(
+    _call("indexer_q_rope_quant", q.device, stream,
         q.data_ptr(), q.stride(0), q.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], weights.data_ptr(), weights.stride(0), N, H,
         float(softmax_scale), float(head_scale), float(eps), q_fp8.data_ptr(), q_fp8.stride(0),
-        q_fp8.stride(1), weights_out.data_ptr(), weights_out.stride(0), _stream(q.device, stream))
-    check("indexer_q_rope_quant", rc)
+        q_fp8.stride(1), weights_out.data_ptr(), weights_out.stride(0))
