@@ -940,7 +940,7 @@ struct IdxParams {
   int64_t wo_st;
 };
 
-constexpr int kIdxRounds = 2;    // items per wave (2 timed best of 1, 2, 3, 4, 8)
+constexpr int kIdxRounds = 2;    // items per wave (2 timed best of 1 to 4)
 
 constexpr int kRowRor8 = 0x128;  // lane i <- lane i^8 within the row (rotate by 8 of 16)
 
