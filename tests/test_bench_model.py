@@ -67,3 +67,12 @@ def test_metric_names_the_headline_workload():
     metric = json.loads(re.search(r'"metric": ("[^"]*")', src).group(1))
     assert metric == ("achieved HBM GB/s (% of peak) + tokens/s, "
                       "inv_rope_fp8_quant 16k tok×32 heads")
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
