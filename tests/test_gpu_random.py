@@ -187,3 +187,38 @@ def test_calls_run_in_order_on_the_callers_stream():
     eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, 8)
     assert_bits_equal(host(sc), es, "side-stream scales")
     assert_codes_match(host(out), eo, "side-stream codes")
+
+
+def test_concurrent_callers_on_their_own_streams():
+    # The library keeps no per-call state: host threads calling it at once
+    # (ctypes drops the GIL for the call), each on its own stream and buffers,
+    # all get their own results.
+    import threading
+    cases = []
+    for i in range(4):
+        cfg = dict(synth.IRQ_TINY, N=64 + 16 * i, H=16, hpg=8, max_pos=65536, seed=610 + i)
+        o, pos, cache = synth.irq_inputs(cfg)
+        out, sc = rq.empty_inv_rope_fp8_quant_outputs(cfg["N"], 16, 8, DEV)
+        cases.append((o, pos, cache, dev(o), dev(pos), dev(cache), out, sc, torch.cuda.Stream()))
+    errors = []
+
+    def worker(case):
+        o, pos, cache, od, pd, cd, out, sc, stream = case
+        try:
+            for _ in range(20):
+                rq.inv_rope_fp8_quant(od, pd, cd, 8, out, sc, stream=stream)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    print("[case] 4 threads x 20 calls, one stream each", flush=True)
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for o, pos, cache, _, _, _, out, sc, _ in cases:
+        eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, 8)
+        assert_bits_equal(host(sc), es, "concurrent scales")
+        assert_codes_match(host(out), eo, "concurrent codes")
