@@ -166,6 +166,97 @@ def test_indexer_random(case):
     assert_codes_match(host(q8), ec, "random indexer codes")
 
 
+@pytest.mark.parametrize("case", range(9))
+def test_fused_forms_random(case):
+    # The fused kernels split one grid at q_waves; ragged q-unit counts put q
+    # and kv work in neighbouring waves.  Each fused form must equal its two
+    # separate calls bit for bit, and the oracle.
+    rng = np.random.default_rng([700, case])
+    N = int(rng.integers(1, 150))
+    Hq = int(rng.integers(1, 11))
+    Hpad = Hq + int(rng.choice([0, 1, 2, 5]))
+    form = ("quant", "full_fp8", "full_bf16")[case % 3]
+    fmt = FMTS[(case // 3) % 2]
+    thr = THREADS[case % 4]
+    weighted = case % 2 == 0
+    print(f"[case] fused random #{case}: form={form} N={N} Hq={Hq} Hpad={Hpad} fmt={fmt} "
+          f"threads={thr} weight={weighted}", flush=True)
+    rq.set_block_threads(thr)
+    q = synth.normal_bf16((N, Hq, 512), 710 + case, synth.T_Q, std=2.0)
+    w = synth.uniform_bf16((512,), 710 + case, synth.T_W, 0.5, 1.5) if weighted else None
+    kv = synth.normal_bf16((N, 512), 710 + case, synth.T_KV)
+    pos = rng.integers(0, 4096, N).astype(np.int64)
+    cache = synth.cos_sin_cache(4096)
+    bs, nb = 16, -(-N // 16) + 2
+    slots = synth.slot_permutation(N, nb * bs, 710 + case)
+    slots[rng.random(N) < 0.1] = -1
+    qd, wd, kd, pd, cd, sd = dev(q), None if w is None else dev(w), dev(kv), dev(pos), dev(cache), dev(slots)
+    if form == "quant":
+        outs = []
+        for fused in (True, False):
+            q_out = torch.full((N, Hpad, 512), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            k_cache = rq.empty_kv_cache(nb, bs, DEV, fill=0xAA)
+            if fused:
+                rq.qnorm_rope_kv_rope_quant_insert(qd, wd, kd, pd, cd, sd, q_out, k_cache, bs,
+                                                   1e-6, fmt)
+            else:
+                rq.qnorm_rope(qd, wd, pd, cd, q_out, 1e-6)
+                rq.kv_rope_quant_insert(kd, pd, cd, sd, k_cache, bs, fmt)
+            torch.cuda.synchronize()
+            outs.append((host(q_out), host(k_cache)))
+        assert_bits_equal(outs[0][0], outs[1][0], "fused vs separate q_out")
+        assert_bits_equal(outs[0][1], outs[1][1], "fused vs separate k_cache")
+        eq, ek = oracle.qnorm_rope_kv_rope_quant_insert(
+            q, w, kv, pos, cache, slots, np.full((nb, bs * 528), 0xAA, np.uint8), Hpad, bs,
+            1e-6, FMT[fmt])
+        assert_bits_equal(outs[0][0], eq, "fused q_out vs oracle")
+        rec = np.zeros(ek.size, bool)
+        for s_ in slots[slots >= 0]:
+            rec[(s_ // bs) * bs * 528 + (s_ % bs) * 528:][:512] = True
+        rec = rec.reshape(ek.shape)
+        got = outs[0][1]
+        assert (got[~rec] == ek[~rec]).all(), "fused cache bytes outside the codes differ"
+        assert_codes_match(got[rec], ek[rec], "fused cache codes vs oracle")
+        return
+    ns = nb * bs
+    full = []
+    for fused in (True, False):
+        cache_full = torch.full((ns, 512), -21846, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        if form == "full_fp8":
+            codes, sc = rq.empty_qnorm_rope_fp8_outputs(N, Hpad, DEV, fmt)
+            if fused:
+                rq.qnorm_rope_fp8_kv_rope_insert_full(qd, wd, kd, pd, cd, sd, codes, sc,
+                                                      cache_full, 1e-6, fmt)
+            else:
+                rq.qnorm_rope_fp8(qd, wd, pd, cd, codes, sc, 1e-6, fmt)
+                rq.kv_rope_insert_full(kd, pd, cd, sd, cache_full)
+            torch.cuda.synchronize()
+            full.append((host(codes), host(sc), host(cache_full)))
+        else:
+            # q in place: needs Hpad == Hq and a contiguous q
+            qi = dev(q)
+            hp = Hq
+            if fused:
+                rq.qnorm_rope_kv_rope_insert_full(qi, wd, kd, pd, cd, sd, qi, cache_full, 1e-6)
+            else:
+                rq.qnorm_rope(qi, wd, pd, cd, qi, 1e-6)
+                rq.kv_rope_insert_full(kd, pd, cd, sd, cache_full)
+            torch.cuda.synchronize()
+            full.append((host(qi), None, host(cache_full)))
+    for a, b, what in zip(full[0], full[1], ("q", "q scales", "kv cache")):
+        if a is not None:
+            assert_bits_equal(a, b, f"fused vs separate {what}")
+    ef = oracle.kv_rope_insert_full(kv, pos, cache, slots, np.full((ns, 512), 0xAAAA, np.uint16))
+    assert_bits_equal(full[0][2], ef, "fused kv cache vs oracle")
+    if form == "full_fp8":
+        ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, Hpad, 1e-6, FMT[fmt])
+        assert_bits_equal(full[0][1], es, "fused q scales vs oracle")
+        assert_codes_match(full[0][0], ec, "fused q codes vs oracle")
+    else:
+        assert_bits_equal(full[0][0], oracle.qnorm_rope(q, w, pos, cache, hp, 1e-6),
+                          "fused in-place q vs oracle")
+
+
 def test_calls_run_in_order_on_the_callers_stream():
     # Work is enqueued on the stream passed in: a long fill queued first on a
     # side stream must finish before the op reads its input there, and the
