@@ -44,14 +44,22 @@ def _fmt(scale_fmt):
 
 
 def _cuda(t, name):
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
 
 
 def _same_device(ref, *named):
+    # device indices as ints: cheaper than building torch.device objects, and
+    # a CPU tensor (index -1) fails too
+    d = ref.get_device()
     for t, name in named:
-        if t is not None and t.device != ref.device:
+        if t is not None and t.get_device() != d:
             raise ValueError(f"{name} must be on {ref.device}")
+
+
+# torch's handle of the current stream of a device, without building a Stream
+# object (falls back to the public API where this build lacks it)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _call(name, device, stream, *args):
@@ -59,16 +67,22 @@ def _call(name, device, stream, *args):
     of `device`), with `device` current during the call, and raise on a
     non-OK status.  The library launches on the current HIP device, so a
     stream or tensors on another device would hand it foreign pointers."""
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    if s.device != device:
-        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
-    fn = getattr(lib(), name)
-    if device.index is not None and device.index != torch.cuda.current_device():
-        with torch.cuda.device(device):
-            rc = fn(*args, s.cuda_stream)
+    idx = device.index
+    if stream is None:
+        handle = (_raw_stream(idx) if _raw_stream is not None
+                  else torch.cuda.current_stream(device).cuda_stream)
     else:
-        rc = fn(*args, s.cuda_stream)
-    check(name, rc)
+        if stream.device != device:
+            raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+        handle = stream.cuda_stream
+    fn = getattr(lib(), name)
+    if idx != torch.cuda.current_device():
+        with torch.cuda.device(idx):
+            rc = fn(*args, handle)
+    else:
+        rc = fn(*args, handle)
+    if rc:
+        check(name, rc)
 
 
 def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
@@ -135,14 +149,14 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
     fmt = _fmt(scale_fmt)
     N, H, hpg, G = _check_o(o, heads_per_group)
     _check_rope_inputs(positions, cos_sin_cache, N)
-    if out.dtype not in _BYTE_DTYPES or tuple(out.shape) != (G, N, hpg * 512) or (
+    if out.dtype not in _BYTE_DTYPES or out.shape != (G, N, hpg * 512) or (
             out.stride(2) != 1):
         raise ValueError(f"out must be uint8/float8_e4m3fn [{G}, {N}, {hpg * 512}], last dim "
                          "contiguous")
     if fmt == RQ_SCALE_UE8M0:
-        if scales.dtype not in _WORD_DTYPES or tuple(scales.shape) != (G, N, hpg):
+        if scales.dtype not in _WORD_DTYPES or scales.shape != (G, N, hpg):
             raise ValueError(f"ue8m0 scales must be int32/uint32 [{G}, {N}, {hpg}]")
-    elif scales.dtype != torch.float32 or tuple(scales.shape) != (G, N, hpg * 4):
+    elif scales.dtype != torch.float32 or scales.shape != (G, N, hpg * 4):
         raise ValueError(f"fp32 scales must be float32 [{G}, {N}, {hpg * 4}]")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"),
                  (scales, "scales"))
@@ -172,7 +186,7 @@ def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None
     and that view of o itself rotates o in place)."""
     N, H, hpg, G = _check_o(o, heads_per_group)
     _check_rope_inputs(positions, cos_sin_cache, N)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (G, N, hpg * 512) or (
+    if out.dtype != torch.bfloat16 or out.shape != (G, N, hpg * 512) or (
             out.stride(2) != 1):
         raise ValueError(f"out must be bf16 [{G}, {N}, {hpg * 512}], last dim contiguous")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"))
@@ -189,7 +203,7 @@ def _check_q_in(q_in, norm_weight, positions, cos_sin_cache):
     N, Hq, _ = q_in.shape
     _check_rope_inputs(positions, cos_sin_cache, N)
     if norm_weight is not None and (norm_weight.dtype != torch.bfloat16
-                                    or tuple(norm_weight.shape) != (512,)
+                                    or norm_weight.shape != (512,)
                                     or not norm_weight.is_contiguous()):
         raise ValueError("norm_weight must be contiguous bf16 [512] or None")
     _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
@@ -205,10 +219,10 @@ def _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq):
     if hpad < Hq:
         raise ValueError("q_head_padded must be >= num_heads_q")
     if fmt == RQ_SCALE_UE8M0:
-        if q_scales.dtype not in _WORD_DTYPES or tuple(q_scales.shape) != (N, hpad) or (
+        if q_scales.dtype not in _WORD_DTYPES or q_scales.shape != (N, hpad) or (
                 not q_scales.is_contiguous()):
             raise ValueError(f"ue8m0 q_scales must be contiguous int32/uint32 [{N}, {hpad}]")
-    elif q_scales.dtype != torch.float32 or tuple(q_scales.shape) != (N, hpad, 4) or (
+    elif q_scales.dtype != torch.float32 or q_scales.shape != (N, hpad, 4) or (
             not q_scales.is_contiguous()):
         raise ValueError(f"fp32 q_scales must be contiguous float32 [{N}, {hpad}, 4]")
     _same_device(q_in, (q_fp8, "q_fp8"), (q_scales, "q_scales"))
@@ -232,7 +246,7 @@ def _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_
         raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
     N = kv.shape[0]
     _check_rope_inputs(positions, cos_sin_cache, N)
-    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
+    if (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (N,)
             or not slot_mapping.is_contiguous()):
         raise ValueError("slot_mapping must be contiguous int64 [N]")
     if k_cache.dtype != torch.uint8 or k_cache.dim() != 2 or k_cache.stride(1) != 1:
@@ -250,7 +264,7 @@ def _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache):
         raise ValueError("kv must be bf16 [N, 512] with a contiguous last dim")
     N = kv.shape[0]
     _check_rope_inputs(positions, cos_sin_cache, N)
-    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,)
+    if (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (N,)
             or not slot_mapping.is_contiguous()):
         raise ValueError("slot_mapping must be contiguous int64 [N]")
     if (cache.dtype != torch.bfloat16 or cache.dim() != 2 or cache.shape[1] < 512
@@ -376,10 +390,10 @@ def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_ou
     N, H, _ = q.shape
     _check_rope_inputs(positions, cos_sin_cache, N)
     for t, name in ((weights, "weights"), (weights_out, "weights_out")):
-        if (t.dtype != torch.float32 or tuple(t.shape) != (N, H)
+        if (t.dtype != torch.float32 or t.shape != (N, H)
                 or (H > 1 and t.stride(1) != 1)):
             raise ValueError(f"{name} must be float32 [N, H] with contiguous heads")
-    if q_fp8.dtype not in _BYTE_DTYPES or tuple(q_fp8.shape) != (N, H, 128) or (
+    if q_fp8.dtype not in _BYTE_DTYPES or q_fp8.shape != (N, H, 128) or (
             q_fp8.stride(2) != 1):
         raise ValueError("q_fp8 must be uint8/float8_e4m3fn [N, H, 128], last dim contiguous")
     _same_device(q, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
