@@ -18,15 +18,32 @@ _LIB = None
 SCALE_FP32 = 0
 SCALE_UE8M0 = 1
 RECORD_BYTES = 528
+# RMSNorm summation orders: "index" is the definition (left to right over the
+# 512 dims); "tree" adds the same squares in a fixed 64-chunk tree.
+SUM_ORDERS = {"index": 0, "tree": 1}
+
+
+def _order(sum_order):
+    if sum_order not in SUM_ORDERS:
+        raise ValueError(f"sum_order must be one of {sorted(SUM_ORDERS)}")
+    return SUM_ORDERS[sum_order]
+
+
+# A test may point the wrapper at another build of oracle.c (the mutation
+# check builds altered copies and expects the pins to fail on each).
+LIB_ENV = "ROPEQUANT_ORACLE_LIB"
 
 
 def lib():
     """Load the compiled oracle, compiling it first if it is not there."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get(LIB_ENV)
+        if path is None:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f32.restype = ctypes.c_float
@@ -46,20 +63,23 @@ def lib():
         L.orc_rope_head.restype = None
         L.orc_quant_head.argtypes = [P, ctypes.c_int, ctypes.c_float, P, P, P]
         L.orc_quant_head.restype = None
-        L.orc_rmsnorm_head.argtypes = [P, P, ctypes.c_float, P]
-        L.orc_rmsnorm_head.restype = None
+        for nm in ("orc_rmsnorm_head", "orc_rmsnorm_head_tree"):
+            getattr(L, nm).argtypes = [P, P, ctypes.c_float, P]
+            getattr(L, nm).restype = None
         L.orc_inv_rope_fp8_quant.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, I32, D,
                                              P, I64, I64, P, I64, I64, I64]
         L.orc_inv_rope_fp8_quant.restype = ctypes.c_int
-        L.orc_qnorm_rope.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, P]
+        L.orc_qnorm_rope.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, P, I32]
         L.orc_qnorm_rope.restype = ctypes.c_int
+        L.orc_qnorm_rope_f32.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, D, P, I32]
+        L.orc_qnorm_rope_f32.restype = ctypes.c_int
         L.orc_kv_rope_quant_insert.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64, I32,
                                                I32, D]
         L.orc_kv_rope_quant_insert.restype = ctypes.c_int
         L.orc_inv_rope_bf16.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, P, I64, I64]
         L.orc_inv_rope_bf16.restype = ctypes.c_int
         L.orc_qnorm_rope_fp8.argtypes = [P, I64, I64, P, P, P, I64, I64, I32, I32, D, I32, D,
-                                         P, P]
+                                         P, P, I32]
         L.orc_qnorm_rope_fp8.restype = ctypes.c_int
         L.orc_kv_rope_insert_full.argtypes = [P, I64, P, P, I64, P, I64, P, I64, I64]
         L.orc_kv_rope_insert_full.restype = ctypes.c_int
@@ -162,11 +182,13 @@ def quant_head(x, scale_fmt=SCALE_FP32, eps=1e-10):
     return codes, sc, int(word[0])
 
 
-def rmsnorm_head(x, weight_bits, eps):
+def rmsnorm_head(x, weight_bits, eps, sum_order="index"):
+    """RMSNorm of one 512-dim fp32 head; the squares are added in `sum_order`."""
     x = _need(np.ascontiguousarray(x, dtype=np.float32), np.float32, "x")
     w = None if weight_bits is None else np.ascontiguousarray(weight_bits, dtype=np.uint16)
     y = np.empty(512, dtype=np.float32)
-    lib().orc_rmsnorm_head(_ptr(x), _ptr(w), float(np.float32(eps)), _ptr(y))
+    fn = lib().orc_rmsnorm_head_tree if _order(sum_order) else lib().orc_rmsnorm_head
+    fn(_ptr(x), _ptr(w), float(np.float32(eps)), _ptr(y))
     return y
 
 
@@ -240,8 +262,10 @@ def inv_rope_bf16(o_bits, positions, cos_sin_cache, heads_per_group, layout="gro
     return out
 
 
-def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps):
-    """Oracle QNR: q_bits uint16 [N, Hq, 512] -> q_out uint16 [N, Hpad, 512]."""
+def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps,
+               sum_order="index"):
+    """Oracle QNR: q_bits uint16 [N, Hq, 512] -> q_out uint16 [N, Hpad, 512].
+    sum_order: "index" (the RMSNorm definition) or "tree" (see SUM_ORDERS)."""
     q_bits = _need(q_bits, np.uint16, "q_in")
     positions = _need(positions, np.int64, "positions")
     cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
@@ -252,13 +276,31 @@ def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps
     q_out = np.full((N, q_head_padded, 512), 0xFFFF, dtype=np.uint16)
     rc = lib().orc_qnorm_rope(_ptr(q_bits), Hq * 512, 512, _ptr(weight_bits), _ptr(positions),
                               _ptr(cos_sin_cache), cos_sin_cache.shape[0], N, Hq,
-                              q_head_padded, eps, _ptr(q_out))
+                              q_head_padded, eps, _ptr(q_out), _order(sum_order))
     _check(rc, "qnorm_rope")
     return q_out
 
 
+def qnorm_rope_f32(q_bits, weight_bits, positions, cos_sin_cache, eps, sum_order="index"):
+    """The fp32 values the q paths round (RMSNorm, then forward RoPE): float32
+    [N, Hq, 512] for the live heads of q_bits uint16 [N, Hq, 512]."""
+    q_bits = _need(q_bits, np.uint16, "q_in")
+    positions = _need(positions, np.int64, "positions")
+    cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")
+    if weight_bits is not None:
+        weight_bits = _need(weight_bits, np.uint16, "weight")
+    N, Hq, D = q_bits.shape
+    assert D == 512
+    z = np.empty((N, Hq, 512), dtype=np.float32)
+    rc = lib().orc_qnorm_rope_f32(_ptr(q_bits), Hq * 512, 512, _ptr(weight_bits),
+                                  _ptr(positions), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                  N, Hq, eps, _ptr(z), _order(sum_order))
+    _check(rc, "qnorm_rope_f32")
+    return z
+
+
 def qnorm_rope_fp8(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps,
-                   scale_fmt=SCALE_FP32, quant_eps=1e-10):
+                   scale_fmt=SCALE_FP32, quant_eps=1e-10, sum_order="index"):
     """Oracle q path into FP8: q_bits uint16 [N, Hq, 512] -> (codes uint8
     [N, Hpad, 512], scales f32 [N, Hpad, 4] or, UE8M0, uint32 [N, Hpad])."""
     q_bits = _need(q_bits, np.uint16, "q_in")
@@ -276,7 +318,7 @@ def qnorm_rope_fp8(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded,
     rc = lib().orc_qnorm_rope_fp8(_ptr(q_bits), Hq * 512, 512, _ptr(weight_bits),
                                   _ptr(positions), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
                                   N, Hq, q_head_padded, eps, scale_fmt, quant_eps, _ptr(codes),
-                                  _ptr(sc))
+                                  _ptr(sc), _order(sum_order))
     _check(rc, "qnorm_rope_fp8")
     return codes, sc
 
@@ -370,9 +412,10 @@ def indexer_q_rope_quant(q_bits, positions, cos_sin_cache, weights, softmax_scal
 def qnorm_rope_kv_rope_quant_insert(q_bits, weight_bits, kv_bits, positions, cos_sin_cache,
                                     slot_mapping, k_cache, q_head_padded, cache_block_size,
                                     eps=1e-6, scale_fmt=SCALE_FP32, quant_eps=1e-10,
-                                    block_stride_bytes=None):
+                                    block_stride_bytes=None, sum_order="index"):
     """The fused op is, by definition, both ops on the same positions."""
-    q_out = qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps)
+    q_out = qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps,
+                       sum_order)
     kv_rope_quant_insert(kv_bits, positions, cos_sin_cache, slot_mapping, k_cache,
                          cache_block_size, block_stride_bytes, scale_fmt, quant_eps)
     return q_out, k_cache

@@ -90,8 +90,9 @@ float orc_e4m3_to_f32(uint8_t c) {
 }
 
 /* fp32 -> e4m3, round to nearest, ties to even mantissa.  Domain: finite
- * |v| <= 448 (callers clamp first, so a NaN code is never produced).  The
- * sign is kept for zero and for values that round to zero.
+ * |v| <= 448 (callers clamp first), and NaN, which takes the format's NaN
+ * code with its sign (S.1111.111).  The sign is kept for zero and for values
+ * that round to zero.
  *
  * Method, straight from the format: find the spacing q of e4m3 values in the
  * binade of |v| (2^-9 below the smallest normal 2^-6, else 2^(e-3) for
@@ -105,6 +106,7 @@ uint8_t orc_f32_to_e4m3(float v) {
   int e, subnormal;
   float n, fl, frac;
   uint32_t code;
+  if (a != a) return (uint8_t)((sign << 7) | 0x7Fu);
   if (a == 0.0f) return (uint8_t)(sign << 7);
   if (a < ldexpf(1.0f, -6)) {
     subnormal = 1;
@@ -174,6 +176,9 @@ void orc_rope_head(const float* x, float* y, const float* cs_row, int inverse) {
  *   UE8M0 scale: t = m_b / 448;  k = ceil(log2 t) exactly;  s_b = 2^k;
  *                v = x * 2^-k (exact)                 ([P4] section 3, [P5])
  *   v is clamped to [-448, 448], then encoded e4m3 RNE.
+ * A block whose values overflowed fp32 (amax = +inf) follows the same
+ * formulas in IEEE arithmetic: FP32 s = +inf and inv = 0; UE8M0 k = 128,
+ * s = +inf, 2^-k = 2^-128 and exponent byte 0xFF.
  * Reading: the quotient x / s is taken as x * (1/s) with 1/s rounded once
  * per block; the pages do not show which form the kernel uses.
  * Outputs: codes[512]; scales_f32[4] (FP32 mode: s_b; UE8M0 mode: 2^k);
@@ -214,17 +219,40 @@ void orc_quant_head(const float* x, int scale_fmt, float eps, uint8_t* codes,
 /* ------------------------------------------------------------- RMSNorm */
 
 /* Per-head RMSNorm over the 512 dims ([P3] section 5 formula:
- * y = x * rsqrt(mean(x^2) + eps) * w).
- * Reading of the unstated sum order (a fixed tree, so results are exact):
+ * y = x * rsqrt(mean(x^2) + eps) * w), read plainly in fp32:
+ *   ss = x_0^2 + x_1^2 + ... + x_511^2, added left to right in index order,
+ *        each square and each sum rounded;
+ *   mean = ss / 512 (exact: a power of two);
+ *   r = 1 / sqrt(mean + eps)  (correctly rounded sqrt, then divide);
+ *   y_d = (x_d * r) * w_d, or x_d * r when there is no weight.
+ * The pages fix no summation order; index order is the plain reading of
+ * "mean(x^2)".  orc_rmsnorm_head_tree below differs only in that order. */
+static void rms_apply(const float* x, const uint16_t* weight, float eps, float ss, float* y) {
+  int d;
+  float mean = ss / 512.0f;
+  float r = 1.0f / sqrtf(mean + eps);
+  for (d = 0; d < HEAD_DIM; ++d) {
+    float v = x[d] * r;
+    y[d] = weight ? v * orc_bf16_to_f32(weight[d]) : v;
+  }
+}
+
+void orc_rmsnorm_head(const float* x, const uint16_t* weight, float eps, float* y) {
+  int d;
+  float ss = x[0] * x[0];
+  for (d = 1; d < HEAD_DIM; ++d) ss = ss + x[d] * x[d];
+  rms_apply(x, weight, eps, ss, y);
+}
+
+/* The same RMSNorm with the squares added in another fixed order, a tree:
  *   p_c = ((x_{8c}^2 + x_{8c+1}^2) + ...) + x_{8c+7}^2   for c = 0..63
  *   for k = 1, 2, 4, 8, 16, 32:  p_c <- p_c + p_{c xor k}  (all c at once)
- *   ss = p_0;  mean = ss * (1/512) (exact);
- *   r = 1 / sqrt(mean + eps)  (correctly rounded sqrt, then divide)
- *   y_d = (x_d * r) * w_d, or x_d * r when there is no weight. */
-void orc_rmsnorm_head(const float* x, const uint16_t* weight, float eps, float* y) {
+ *   ss = p_0.
+ * Not the definition: a second rounding order of the same sum, for tests
+ * that separate the summation order from every other step. */
+void orc_rmsnorm_head_tree(const float* x, const uint16_t* weight, float eps, float* y) {
   float p[64], t[64];
   int c, d, k;
-  float ss, mean, r;
   for (c = 0; c < 64; ++c) {
     float acc = x[8 * c] * x[8 * c];
     for (d = 1; d < 8; ++d) acc = acc + x[8 * c + d] * x[8 * c + d];
@@ -234,13 +262,16 @@ void orc_rmsnorm_head(const float* x, const uint16_t* weight, float eps, float* 
     for (c = 0; c < 64; ++c) t[c] = p[c] + p[c ^ k];
     for (c = 0; c < 64; ++c) p[c] = t[c];
   }
-  ss = p[0];
-  mean = ss * (1.0f / 512.0f);
-  r = 1.0f / sqrtf(mean + eps);
-  for (d = 0; d < HEAD_DIM; ++d) {
-    float v = x[d] * r;
-    y[d] = weight ? v * orc_bf16_to_f32(weight[d]) : v;
-  }
+  rms_apply(x, weight, eps, p[0], y);
+}
+
+/* sum_order argument of the q-path ops: ORC_SUM_INDEX is the definition */
+enum { ORC_SUM_INDEX = 0, ORC_SUM_TREE = 1 };
+
+static void rmsnorm_by_order(const float* x, const uint16_t* weight, float eps, int32_t order,
+                             float* y) {
+  if (order == ORC_SUM_TREE) orc_rmsnorm_head_tree(x, weight, eps, y);
+  else orc_rmsnorm_head(x, weight, eps, y);
 }
 
 /* ------------------------------------------------------ shared validation */
@@ -352,11 +383,13 @@ int orc_inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_strid
  * q_out[N, Hpad, 512] (contiguous); heads Hq..Hpad-1 are written as +0.
  * [P1] section 1 (q_out preallocated, every element written, pad zeroed,
  * q_head_padded >= num_heads_q); [P3] section 5 (RMSNorm).
- * Reading: fp32 throughout, one bf16 rounding at the end. */
+ * Reading: fp32 throughout, one bf16 rounding at the end.
+ * sum_order: ORC_SUM_INDEX (the RMSNorm definition) or ORC_SUM_TREE. */
 int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
                    const uint16_t* norm_weight, const int64_t* positions,
                    const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
-                   int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out) {
+                   int32_t n_heads_q, int32_t q_head_padded, double eps, uint16_t* q_out,
+                   int32_t sum_order) {
   int64_t t;
   int32_t h;
   int d;
@@ -365,6 +398,7 @@ int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
   if (n_tokens < 0 || n_heads_q <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
   if (q_head_padded < n_heads_q) return ORC_ERR_SHAPE;
   if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
   if (n_tokens == 0) return ORC_OK;
   if (!q_in || !positions || !cos_sin_cache || !q_out) return ORC_ERR_NULL;
   for (t = 0; t < n_tokens; ++t)
@@ -378,9 +412,40 @@ int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
         continue;
       }
       load_head(q_in + t * q_stride_token + (int64_t)h * q_stride_head, x);
-      orc_rmsnorm_head(x, norm_weight, epsf, y);
+      rmsnorm_by_order(x, norm_weight, epsf, sum_order, y);
       orc_rope_head(y, z, row, 0);
       for (d = 0; d < HEAD_DIM; ++d) dst[d] = orc_f32_to_bf16(z[d]);
+    }
+  }
+  return ORC_OK;
+}
+
+/* The fp32 values the q paths round: RMSNorm (squares added in sum_order)
+ * then forward RoPE, exactly as orc_qnorm_rope computes them before its bf16
+ * rounding and orc_qnorm_rope_fp8 before its quantization; live heads only,
+ * z[(t*Hq + h)*512 + d].  Tests use them to tell where a rounding decision
+ * sits close to its boundary. */
+int orc_qnorm_rope_f32(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
+                       const uint16_t* norm_weight, const int64_t* positions,
+                       const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
+                       int32_t n_heads_q, double eps, float* z_out, int32_t sum_order) {
+  int64_t t;
+  int32_t h;
+  float x[HEAD_DIM], y[HEAD_DIM];
+  float epsf = (float)eps;
+  if (n_tokens < 0 || n_heads_q <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
+  if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
+  if (n_tokens == 0) return ORC_OK;
+  if (!q_in || !positions || !cos_sin_cache || !z_out) return ORC_ERR_NULL;
+  for (t = 0; t < n_tokens; ++t)
+    if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ERR_VALUE;
+  for (t = 0; t < n_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * ROPE_DIM;
+    for (h = 0; h < n_heads_q; ++h) {
+      load_head(q_in + t * q_stride_token + (int64_t)h * q_stride_head, x);
+      rmsnorm_by_order(x, norm_weight, epsf, sum_order, y);
+      orc_rope_head(y, z_out + (t * n_heads_q + h) * HEAD_DIM, row, 0);
     }
   }
   return ORC_OK;
@@ -390,8 +455,8 @@ int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
 
 /* The q path into a separate FP8 tensor, one of the full-cache variants named
  * beside the op schema in [P1] section 2.  Readings (the pages give only the
- * variant's name): RMSNorm and forward RoPE exactly as in orc_qnorm_rope, in
- * fp32; the fp32 head (not its bf16 rounding: the same fusion as the kv path)
+ * variant's name): RMSNorm (its squares added in sum_order) and forward RoPE
+ * exactly as in orc_qnorm_rope, in fp32; the fp32 head (not its bf16 rounding: the same fusion as the kv path)
  * goes through orc_quant_head; a pad head h in [Hq, Hpad) is a zero head
  * quantized the same way (codes +0, scales from eps).  Layout:
  *   codes   q_fp8[(t*Hpad + h)*512 + d]                          (bytes)
@@ -401,7 +466,7 @@ int orc_qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_s
                        const uint16_t* norm_weight, const int64_t* positions,
                        const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
                        int32_t n_heads_q, int32_t q_head_padded, double eps, int32_t scale_fmt,
-                       double quant_eps, uint8_t* q_fp8, void* q_scales) {
+                       double quant_eps, uint8_t* q_fp8, void* q_scales, int32_t sum_order) {
   int64_t t;
   int32_t h;
   int b;
@@ -413,6 +478,7 @@ int orc_qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_s
   if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
   if (scale_fmt != ORC_SCALE_FP32 && scale_fmt != ORC_SCALE_UE8M0) return ORC_ERR_VALUE;
   if (!eps_ok(quant_eps)) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
   if (n_tokens == 0) return ORC_OK;
   if (!q_in || !positions || !cos_sin_cache || !q_fp8 || !q_scales) return ORC_ERR_NULL;
   for (t = 0; t < n_tokens; ++t)
@@ -423,7 +489,7 @@ int orc_qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_s
       int64_t u = t * q_head_padded + h;
       if (h < n_heads_q) {
         load_head(q_in + t * q_stride_token + (int64_t)h * q_stride_head, x);
-        orc_rmsnorm_head(x, norm_weight, epsf, y);
+        rmsnorm_by_order(x, norm_weight, epsf, sum_order, y);
         orc_rope_head(y, z, row, 0);
       } else {
         memset(z, 0, sizeof z);

@@ -52,6 +52,15 @@ def _brute_force_e4m3(x):
     return (codes[pick] | (sign << 7)).astype(np.uint8)
 
 
+def test_e4m3_encode_nan_takes_the_nan_code_with_its_sign():
+    # NaN (an infinite block maximum times a zero reciprocal) encodes as
+    # S.1111.111, as torch's cast does
+    x = from_bits(np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32))
+    got = oracle.f32_to_e4m3(x)
+    assert (got == np.array([0x7F, 0xFF, 0x7F, 0xFF], np.uint8)).all()
+    assert (got == torch_e4m3(x)).all()
+
+
 def test_e4m3_decode_all_codes_match_torch():
     codes = np.arange(256, dtype=np.uint8)
     mine = oracle.e4m3_to_f32(codes)

@@ -89,6 +89,16 @@ def test_indexer_weight_fold_order():
         # and the order is the printed one: ((w * q) * ss) * hs
         ref = ((np.float32(w) * np.float32(qs)) * np.float32(ss)) * np.float32(hs)
         assert f32_bits(np.float32(w_out)) == f32_bits(ref)
+    # q_scale is a power of two, so only (w * ss) * hs against w * (ss * hs)
+    # can round differently; at w = 0.9, ss = 128^-0.5, hs = 1.7 they do (each
+    # product of two fp32 values is exact in fp64, so every step below is one
+    # fp32 rounding)
+    w, ss, hs = np.float32(0.9), np.float32(128 ** -0.5), np.float32(1.7)
+    _, w_out, qs = oracle.indexer_head(x, row, w, ss, hs)
+    printed = np.float32(np.float32(np.float32(w * qs) * ss) * hs)
+    other = np.float32(w * np.float32(qs * np.float32(ss * hs)))
+    assert printed != other
+    assert f32_bits(np.float32(w_out)) == f32_bits(printed)
 
 
 def test_indexer_zero_head_uses_eps_floor():

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from rope_fp8_quant_amd import synth
-from tests.helpers import bf16_value, e4m3_ulp, f32_bits, rope_angles
+from tests.helpers import bf16_value, e4m3_ulp, f32_bits, rope_angles, torch_bf16
 
 
 def _identity_cache(max_pos):
@@ -146,6 +146,35 @@ def test_qnr_end_to_end_fp64_within_one_bf16_ulp():
             got = bf16_value(out[t, h]).astype(np.float64)
             ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 1e-30))) - 7)
             assert (np.abs(got - y) <= ulp).all()
+
+
+@pytest.mark.parametrize("sum_order", ["index", "tree"])
+def test_qnr_f32_is_what_the_q_paths_round(sum_order):
+    # its bf16 rounding by torch's cast is qnorm_rope's live heads, its block
+    # quantization is qnorm_rope_fp8's, and it agrees with an fp64 evaluation
+    cfg = dict(synth.QNR_FORWARD, N=5, Hq=6, Hpad=8)
+    q, w, pos, cache = synth.qnr_inputs(cfg)
+    z = oracle.qnorm_rope_f32(q, w, pos, cache, 1e-6, sum_order)
+    out = oracle.qnorm_rope(q, w, pos, cache, 8, 1e-6, sum_order)
+    assert (torch_bf16(z) == out[:, :6]).all()
+    codes, sc = oracle.qnorm_rope_fp8(q, w, pos, cache, 8, 1e-6, sum_order=sum_order)
+    for t in range(5):
+        for h in range(6):
+            c, s, _ = oracle.quant_head(z[t, h])
+            assert (c == codes[t, h]).all() and (f32_bits(s) == f32_bits(sc[t, h])).all()
+    ang = rope_angles(pos)
+    wf = bf16_value(w).astype(np.float64)
+    x = bf16_value(q).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + 1e-6)
+    y = x * r * wf
+    zr = (y[..., 448::2] + 1j * y[..., 449::2]) * np.exp(1j * ang)[:, None, :]
+    pair = np.repeat(np.abs(y[..., 448::2]) + np.abs(y[..., 449::2]), 2, axis=-1)
+    y[..., 448::2], y[..., 449::2] = zr.real, zr.imag
+    # a few fp32 roundings of each value; a rotated value's roundings are
+    # relative to its pair's magnitude (the products may cancel)
+    tol = np.abs(y) * 2.0 ** -18
+    tol[..., 448:] += 2.0 ** -18 * pair
+    assert (np.abs(z - y) <= tol).all()
 
 
 def test_qnr_null_weight_is_unit_weight():

@@ -166,6 +166,34 @@ def test_quant_zero_block_uses_eps():
     assert (codes[128:256] == 0x80).all()
 
 
+@pytest.mark.parametrize("scale_fmt", [oracle.SCALE_FP32, oracle.SCALE_UE8M0])
+def test_quant_overflowed_block(scale_fmt):
+    # Block 3 holds +inf (a rotated pair that overflowed fp32); the other
+    # blocks are unaffected.  IEEE arithmetic on the same formulas: FP32 gives
+    # s = inf / 448 = inf and 1/s = 0, so finite values encode as signed
+    # zeros and the infinity as NaN (inf * 0); UE8M0 gives k = 128, s = 2^128
+    # = inf and exponent byte 0xFF, and the finite values are scaled by the
+    # exact 2^-128 (the infinity clamps to 448).
+    x = _head(31, std=1e30)
+    x[500] = np.inf
+    codes, sc, word = oracle.quant_head(x, scale_fmt)
+    ref_c, ref_s, ref_w = oracle.quant_head(np.where(np.arange(512) < 384, x, 1.0)
+                                            .astype(np.float32), scale_fmt)
+    assert (codes[:384] == ref_c[:384]).all() and (sc[:3] == ref_s[:3]).all()
+    assert sc[3] == np.inf
+    blk = x[384:]
+    if scale_fmt == oracle.SCALE_FP32:
+        fin = np.isfinite(blk)
+        assert (codes[384:][fin] == np.where(np.signbit(blk[fin]), 0x80, 0x00)).all()
+        assert codes[500] & 0x7F == 0x7F  # NaN code
+    else:
+        assert (word >> 24) == 0xFF and (word & 0xFFFFFF) == (ref_w & 0xFFFFFF)
+        scaled = blk.astype(np.float64) * 2.0 ** -128  # exact
+        exp = torch_e4m3(np.clip(scaled, -448, 448).astype(np.float32))
+        assert (codes[384:] == exp).all()
+        assert codes[500] == 0x7E
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_quant_ue8m0_properties(seed):
     x = _head(seed, std=3.0)
@@ -196,12 +224,13 @@ def _rms64(x, w, eps):
     return x * r * (1.0 if w is None else bf16_value(w).astype(np.float64))
 
 
+@pytest.mark.parametrize("sum_order", ["index", "tree"])
 @pytest.mark.parametrize("eps", [1e-6, 0.5])
-def test_rmsnorm_matches_fp64(eps):
+def test_rmsnorm_matches_fp64(eps, sum_order):
     w = synth.uniform_bf16((512,), 3, synth.T_W, 0.5, 1.5)
     for seed in range(8):
         x = _head(seed, std=2.0)
-        y = oracle.rmsnorm_head(x, w, eps).astype(np.float64)
+        y = oracle.rmsnorm_head(x, w, eps, sum_order=sum_order).astype(np.float64)
         ref = _rms64(x, w, eps)
         assert (np.abs(y - ref) <= 4e-6 * np.abs(ref) + 1e-30).all()
 
@@ -222,23 +251,58 @@ def test_rmsnorm_null_weight_equals_unit_weight():
     assert (f32_bits(a) == f32_bits(b)).all()
 
 
-def test_rmsnorm_sum_order_hand_derived():
+def _r_of_ss(ss, eps=1e-6):
+    """r for a given fp32 sum of squares, each step one fp32 rounding."""
+    mean = np.float32(ss) / np.float32(512.0)
+    return np.float32(1.0) / np.sqrt(mean + np.float32(eps), dtype=np.float32)
+
+
+def test_rmsnorm_index_order_hand_derived():
+    # x = [2^12, 1 x 511].  Left to right, 2^24 + 1 lies halfway between 2^24
+    # and 2^24 + 2 and rounds to the even 2^24, so each of the 511 additions
+    # leaves 2^24: ss = 2^24.  The exact sum is 2^24 + 511; summed right to
+    # left it is 2^24 + 512 (511 + 2^24 ties to the even 2^24 + 512); the
+    # 64-chunk tree gives 2^24 + 504 (chunk 0 stays 2^24, the other 63 chunks
+    # are exact 8s that the butterflies add exactly).
+    x = np.ones(512, np.float32)
+    x[0] = 2.0 ** 12
+    y = oracle.rmsnorm_head(x, None, 1e-6)
+    r = _r_of_ss(2.0 ** 24)
+    assert f32_bits(y[1]) == f32_bits(r)
+    assert f32_bits(y[0]) == f32_bits(np.float32(2.0 ** 12) * r)
+    for other in (2.0 ** 24 + 511, 2.0 ** 24 + 512, 2.0 ** 24 + 504):
+        assert _r_of_ss(other) != r  # the case tells the orders apart
+    yt = oracle.rmsnorm_head(x, None, 1e-6, sum_order="tree")
+    assert f32_bits(yt[1]) == f32_bits(_r_of_ss(2.0 ** 24 + 504))
+
+
+def test_rmsnorm_tree_order_hand_derived():
     # Chunk 0 = [2^12, 1 x 7]: left to right, 2^24 + 1 rounds back to 2^24
     # (tie to even) seven times -> 2^24.  Chunks 2 and 3 each hold [1, 0 x 7].
     # Butterfly k=1 gives chunk0+chunk1 = 2^24 and chunk2+chunk3 = 2; k=2 adds
-    # them: 2^24 + 2 exactly.  (Left-to-right over all 512 dims would give
-    # 2^24; summing chunk 0 right-to-left would give 2^24 + 8.)
+    # them: 2^24 + 2 exactly.  (Left-to-right over all 512 dims gives 2^24;
+    # summing chunk 0 right-to-left would give 2^24 + 8.)
     x = np.zeros(512, np.float32)
     x[0] = 2.0 ** 12
     x[1:8] = 1.0
     x[16] = 1.0
     x[24] = 1.0
-    ss = np.float32(2.0 ** 24 + 2)
-    mean = ss * np.float32(1.0 / 512.0)
-    r = np.float32(1.0) / np.sqrt(mean + np.float32(1e-6), dtype=np.float32)
-    y = oracle.rmsnorm_head(x, None, 1e-6)
+    r = _r_of_ss(2.0 ** 24 + 2)
+    y = oracle.rmsnorm_head(x, None, 1e-6, sum_order="tree")
     assert f32_bits(y[1]) == f32_bits(np.float32(1.0) * r)
-    ss_wrong = np.float32(2.0 ** 24)
-    r_wrong = np.float32(1.0) / np.sqrt(ss_wrong * np.float32(1 / 512) + np.float32(1e-6),
-                                        dtype=np.float32)
-    assert r != r_wrong  # the test can tell the orders apart
+    r_index = _r_of_ss(2.0 ** 24)
+    assert r != r_index  # the test can tell the orders apart
+    assert f32_bits(oracle.rmsnorm_head(x, None, 1e-6)[1]) == f32_bits(r_index)
+
+
+@pytest.mark.parametrize("sum_order", ["index", "tree"])
+def test_rmsnorm_orders_exact_on_exact_sums(sum_order):
+    # Small integers: every square and every partial sum is an exact fp32
+    # integer, so any order gives the exact sum, and both orders agree bit for
+    # bit with each other and with the fp64 closed form rounded per step.
+    rng = np.random.default_rng(5)
+    for _ in range(4):
+        x = rng.integers(-8, 9, 512).astype(np.float32)
+        ss = float(np.sum(x.astype(np.float64) ** 2))
+        y = oracle.rmsnorm_head(x, None, 1e-6, sum_order=sum_order)
+        assert (f32_bits(y) == f32_bits(x * _r_of_ss(ss))).all()
