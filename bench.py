@@ -1,7 +1,7 @@
 """Benchmark of the fused RoPE + block-FP8 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--only irq|qnr|kvi|idx|variants|decode|copy]
+                    [--only irq|qnr|kvi|idx|variants|decode|copy|stream]
 
 A step is one launch of ``inv_rope_fp8_quant`` over the prefill workload
 (16384 tokens x 32 heads in 4 groups of 8, head dim 512, bf16 in, e4m3 +
@@ -18,7 +18,12 @@ the CPU oracle timed on this host.  The other ops (qnorm_rope and
 kv_rope_quant_insert on the forward workload, their one-launch fusion, the
 indexer query path, the output variants - bf16 inverse RoPE, q to FP8, kv into
 the bf16 token-strided cache and the fused full-cache forms - and decode
-latencies) are timed the same way and reported under "extra".
+latencies) are timed the same way and reported under "extra", beside the
+streaming ceiling of this part for the same access patterns (kernels in
+bench_stream.hip: reads, writes and inv_rope_fp8_quant's byte pattern with no
+arithmetic, and the cost of an empty launch).  Launches too short to time
+through Python (the kv paths on the forward workload, decode) are also timed
+as calls inside a HIP graph.
 """
 import argparse
 import hashlib
@@ -33,6 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+STREAM_SRC = os.path.join(ROOT, "bench_stream.hip")
+STREAM_LIB = os.path.join(ROOT, "bench_stream.so")
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "irq_prefill_n16384_h32_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", "ropequant.hip")
 
@@ -134,6 +141,107 @@ def time_rotating(fns, steps, warmup, stream):
     return time_launches(step, steps, warmup, stream)
 
 
+def build_stream_lib(verbose=False):
+    """Compile the streaming-ceiling kernels (bench_stream.hip) for gfx950."""
+    from rope_fp8_quant_amd import build as lib_build
+    return lib_build.compile_hip(STREAM_SRC, STREAM_LIB, verbose)
+
+
+_stream_lib = None
+
+
+def stream_lib():
+    import ctypes
+    global _stream_lib
+    if _stream_lib is None:
+        if not os.path.exists(STREAM_LIB):
+            build_stream_lib()
+        L = ctypes.CDLL(STREAM_LIB)
+        P, U64, U32, I = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+        L.bench_stream_read.argtypes = [P, U64, U32, P, P]
+        L.bench_stream_write.argtypes = [P, U64, I, P]
+        L.bench_stream_irq.argtypes = [P, P, P, U64, P]
+        L.bench_stream_empty.argtypes = [P]
+        for f in (L.bench_stream_read, L.bench_stream_write, L.bench_stream_irq,
+                  L.bench_stream_empty):
+            f.restype = I
+        _stream_lib = L
+    return _stream_lib
+
+
+def _ok(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: launch refused")
+
+
+def bench_stream(args, device, stream):
+    """What HBM sustains on this part for the kernels' access patterns, with
+    no arithmetic: 512 MiB of 1 KiB rows read (nontemporal), written
+    (nontemporal, plain, sc1), and inv_rope_fp8_quant's traffic for the
+    prefill workload's 524288 units; each over rotating buffers like the
+    kernels.  Also the fixed cost of one empty launch, eager and in a graph."""
+    import torch
+    L = stream_lib()
+
+    def h():  # torch's current stream (a graph's capture stream while capturing)
+        return torch.cuda.current_stream().cuda_stream
+    res = {}
+    rows = 1 << 19  # 512 MiB of 1 KiB rows
+    nbytes = rows * 1024
+    sets = rotation_sets(nbytes) + 1
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(i + 1)
+            for i in range(sets)]
+    sink = torch.zeros(64, dtype=torch.int32, device=device)
+    # the XOR of 64 bytes each equal to i+1 is 0 per lane, never 0xDEADBEEF
+    fns = [lambda b=b: _ok(L.bench_stream_read(b.data_ptr(), rows, 0xDEADBEEF, sink.data_ptr(),
+                                               h()), "read") for b in bufs]
+    ms = time_rotating(fns, args.steps, args.warmup, stream)
+    res["read_nt"] = dict(_rate("512 MiB read, 1 KiB rows, nontemporal", ms * 1e3, nbytes),
+                          buffer_sets=sets)
+    for pol, name in ((0, "write_nt"), (1, "write_plain"), (2, "write_sc1")):
+        fns = [lambda b=b, pol=pol: _ok(L.bench_stream_write(b.data_ptr(), rows, pol, h()),
+                                        "write") for b in bufs]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
+        res[name] = dict(_rate(f"512 MiB written, 1 KiB rows, {name[6:]}", ms * 1e3, nbytes),
+                         buffer_sets=sets)
+    del bufs
+    torch.cuda.empty_cache()
+    units = 16384 * 32
+    b = units * (1024 + 512 + 16)
+    sets = rotation_sets(b)
+    rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
+            torch.empty(units * 512, dtype=torch.uint8, device=device),
+            torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
+    fns = [lambda s_=s_, c=c, sc=sc: _ok(L.bench_stream_irq(s_.data_ptr(), c.data_ptr(),
+                                                             sc.data_ptr(), units, h()), "irq")
+           for s_, c, sc in rot]
+    ms = time_rotating(fns, args.steps, args.warmup, stream)
+    res["irq_pattern"] = dict(_rate("inv_rope_fp8_quant's bytes for 16384 x 32 units, no math",
+                                    ms * 1e3, b), buffer_sets=sets)
+    del rot, fns
+    torch.cuda.empty_cache()
+
+    def empty():
+        _ok(L.bench_stream_empty(h()), "empty")
+    res["empty_launch"] = dict(us_eager=round(time_launches(empty, 500, 100, stream) * 1e3, 3),
+                               us_graph=round(graph_per_call_us(empty), 3))
+    return res
+
+
+def graph_rotating_per_call_us(fns, calls=None, replays=5):
+    """Per-call time of launches captured in one HIP graph, call i on buffer
+    set i mod len(fns) (median of `replays` replays): the GPU-side cost of a
+    launch, without Python dispatch, on buffers the previous calls did not
+    touch."""
+    calls = calls or max(100, 2 * len(fns))
+    it = [0]
+
+    def step():
+        fns[it[0] % len(fns)]()
+        it[0] += 1
+    return graph_per_call_us(step, calls, replays)
+
+
 def to_dev(a, device):
     import torch
     a = np.ascontiguousarray(a)
@@ -161,6 +269,26 @@ def bench_irq(args, device, stream, fmt="fp32", same_buffers=False):
     ms = time_rotating(fns, args.steps, args.warmup, stream)
     del rot, fns, od
     return cfg, ms, (o, pos, cache), sets
+
+
+# Filled by bench_stream when it runs: the empty-launch cost in a graph and
+# the streaming rate of inv_rope_fp8_quant's byte pattern, for the estimate
+# beside short launches.
+CEILING = {}
+
+
+def small_launch_record(name, b, us_graph, us_python, sets):
+    """A launch too short to time through Python: `us` is its per-call time in
+    a HIP graph over rotating buffers; beside it the Python-loop time and,
+    when the streaming ceiling was measured, the estimate of an empty launch
+    plus its bytes at the ceiling rate."""
+    rec = dict(_rate(name, us_graph, b), us_python=round(us_python, 3), buffer_sets=sets,
+               timing="per call inside a HIP graph, call i on buffer set i mod buffer_sets")
+    if CEILING:
+        est = CEILING["floor_us"] + b / CEILING["gbs"] / 1e3
+        rec.update(launch_floor_us=CEILING["floor_us"], ceiling_gbs=CEILING["gbs"],
+                   estimate_us=round(est, 3), residual_us=round(us_graph - est, 3))
+    return rec
 
 
 def bench_qnr_kvi(args, device, stream):
@@ -196,9 +324,8 @@ def bench_qnr_kvi(args, device, stream):
         fns = [lambda k=k, s=s, c=c: rq.kv_rope_quant_insert(k, pd, cd, s, c, cfg["block_size"])
                for k, s, c in rot]
         ms = time_rotating(fns, args.steps, args.warmup, stream)
-        res["kv_rope_quant_insert"] = dict(workload=cfg["name"], us=ms * 1e3, bytes=b,
-                                           gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS,
-                                           buffer_sets=sets)
+        res["kv_rope_quant_insert"] = small_launch_record(
+            cfg["name"], b, graph_rotating_per_call_us(fns), ms * 1e3, sets)
         del rot, fns
         # the same q and kv work in one launch (positions 0..8191 serve both)
         qc = synth.QNR_FORWARD
@@ -298,8 +425,9 @@ def bench_variants(args, device, stream):
     rot = [(kd.clone(), torch.empty_like(full)) for _ in range(sets)]
     fns = [lambda k=k, f=f: rq.kv_rope_insert_full(k, pd, cd, sd, f) for k, f in rot]
     ms = time_rotating(fns, args.steps, args.warmup, stream)
-    res["kv_rope_insert_full"] = dict(_rate(f"kvf_forward_n{N}_{ns}slots", ms * 1e3,
-                                            kvf_bytes(N)), buffer_sets=sets)
+    res["kv_rope_insert_full"] = small_launch_record(
+        f"kvf_forward_n{N}_{ns}slots", kvf_bytes(N), graph_rotating_per_call_us(fns), ms * 1e3,
+        sets)
     del rot, fns
     b = qf8_bytes(N, Hq, Hpad) + kvf_bytes(N) - N * 264
     sets = rotation_sets(b)
@@ -569,8 +697,8 @@ def main():
     # from idle, so the timed region starts after 100 untimed launches
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "variants", "decode", "copy"],
-                    default=None)
+    ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "variants", "decode", "copy",
+                                       "stream"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -589,14 +717,26 @@ def main():
     if args.only == "copy":
         print(json.dumps({"copy_calibration": bench_copy(args, device, stream)}))
         return
+    ceiling = None
+    if args.only in (None, "stream", "kvi", "variants"):
+        progress("streaming ceiling")
+        ceiling = bench_stream(args, device, stream)
+        CEILING.update(floor_us=ceiling["empty_launch"]["us_graph"],
+                       gbs=round(ceiling["irq_pattern"]["gbs"], 1))
+        torch.cuda.empty_cache()
+    if args.only == "stream":
+        print(json.dumps({"stream_ceiling": ceiling}))
+        return
     if args.only in ("qnr", "kvi", "idx"):
-        print(json.dumps({"extra": bench_qnr_kvi(args, device, stream)}))
+        print(json.dumps({"extra": bench_qnr_kvi(args, device, stream),
+                          "stream_ceiling": ceiling}))
         return
     if args.only == "decode":
         print(json.dumps({"decode": bench_decode(args, device, stream)}))
         return
     if args.only == "variants":
-        print(json.dumps({"extra": bench_variants(args, device, stream)}))
+        print(json.dumps({"extra": bench_variants(args, device, stream),
+                          "stream_ceiling": ceiling}))
         return
 
     cfg, ms, host_inputs, sets = bench_irq(args, device, stream)
@@ -658,6 +798,9 @@ def main():
         line["cpu_baseline_sharded"] = cpu_baseline_sharded(host_inputs)
     if extra:
         line["extra"] = extra
+    if ceiling:
+        line["stream_ceiling"] = ceiling
+        line["frac_of_stream_ceiling"] = round(gbs / ceiling["irq_pattern"]["gbs"], 4)
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,152 @@
+// Streaming-ceiling kernels for bench.py (measurement only; not part of
+// libropequant's ABI).  They move bytes in the access patterns the library's
+// kernels use, with no arithmetic, so that bench.py can report what this
+// part's HBM actually sustains for each pattern beside what the kernels
+// reach:
+//   * stream_read     - one 1 KiB row per 16-byte-per-lane nontemporal load
+//                       instruction, four rows per wave (the kernels' reads);
+//   * stream_write    - the same rows written with nontemporal, plain or
+//                       sc1-policy (buffer) 16-byte stores;
+//   * stream_irq      - inv_rope_fp8_quant's traffic per 512-dim unit: a 1 KiB
+//                       row read, 512 bytes and one 16-byte scale group
+//                       written, with the same workgroup size (128 threads)
+//                       and XCD chunking (64 workgroups);
+//   * stream_empty    - a launch that does nothing: the fixed cost of one
+//                       launch on a stream.
+// Every kernel covers exactly `rows` rows; the host sizes the grid so that no
+// wave reads or writes past them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t* gptr_c;
+typedef __attribute__((address_space(1))) u32x4_t* gptr;
+
+// Workgroups dealt to the 8 XCDs in chunks of 2^chunk_log2 consecutive ones
+// (a bijection on [0, gridDim.x); a tail shorter than 8 chunks keeps its
+// order), the mapping the library's kernels use.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t chunk_log2) {
+  const uint32_t nb = gridDim.x, b = blockIdx.x;
+  const uint32_t full = (nb >> (chunk_log2 + 3)) << (chunk_log2 + 3);
+  if (b >= full) return b;
+  const uint32_t xcd = b & 7u, local = b >> 3;
+  const uint32_t chunk = local >> chunk_log2, within = local & ((1u << chunk_log2) - 1u);
+  return (((chunk << 3) + xcd) << chunk_log2) + within;
+}
+
+__device__ __forceinline__ uint32_t wave_id(uint32_t chunk_log2) {
+  return __builtin_amdgcn_readfirstlane(xcd_block(chunk_log2) * (blockDim.x >> 6) +
+                                        (threadIdx.x >> 6));
+}
+
+// Reads rows [4w, 4w + 4) of 1 KiB; a value is written to sink only when the
+// XOR of everything read equals `never` (chosen by the host as a value the
+// data cannot produce), which keeps the loads live.
+__global__ __launch_bounds__(256) void stream_read(const uint8_t* src, uint64_t rows,
+                                                   uint32_t never, uint32_t* sink) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t r0 = (uint64_t)wave_id(4) * 4;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r0 + k < rows)
+      acc ^= __builtin_nontemporal_load((gptr_c)(src + (r0 + k) * 1024 + 16 * lane));
+  }
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == never) sink[lane] = x;
+}
+
+// POLICY: 0 nontemporal, 1 plain, 2 sc1 through a buffer store on the row.
+template <int POLICY>
+__global__ __launch_bounds__(256) void stream_write(uint8_t* dst, uint64_t rows, uint32_t v) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t r0 = (uint64_t)wave_id(4) * 4;
+  const u32x4_t w = {v, v ^ lane, v + lane, ~v};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r0 + k >= rows) continue;
+    uint8_t* row = dst + (r0 + k) * 1024;
+    if (POLICY == 0) {
+      __builtin_nontemporal_store(w, (gptr)(row + 16 * lane));
+    } else if (POLICY == 1) {
+      *(gptr)(row + 16 * lane) = w;
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, 1024, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(w, rs, 16 * lane, 0, 16);
+    }
+  }
+}
+
+// Per unit u: read the 1 KiB row u of src; write 512 bytes at codes + 512 u
+// (nontemporal) and 16 bytes at scales + 16 u (plain), as inv_rope_fp8_quant
+// does with group-major outputs.  Four units per wave; lanes 0..31 write units
+// 0 and 2, lanes 32..63 units 1 and 3, 16 bytes each.
+__global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* codes,
+                                                  uint8_t* scales, uint64_t units) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t u0 = (uint64_t)wave_id(6) * 4;
+  u32x4_t in[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t u = u0 + k < units ? u0 + k : units - 1;
+    in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
+  }
+  const uint32_t half = lane >> 5, j = lane & 31;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint64_t u = u0 + 2 * k + half;
+    // something from every row read, so no load is dead
+    const u32x4_t w = in[2 * k + half] ^ in[2 * k + 1 - half];
+    if (u < units) __builtin_nontemporal_store(w, (gptr)(codes + u * 512 + 16 * j));
+  }
+  const uint32_t row = lane >> 4;
+  if ((lane & 15) == 0 && u0 + row < units) {
+    const u32x4_t s = in[row];
+    *(gptr)(scales + (u0 + row) * 16) = s;
+  }
+}
+
+__global__ void stream_empty() {}
+
+int grid_for(uint64_t rows_or_units, uint32_t per_block) {
+  return (int)((rows_or_units + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Each returns 0, or -1 when the runtime refuses the launch (or the size is
+// out of range for a 32-bit grid).
+int bench_stream_read(const void* src, uint64_t rows, uint32_t never, void* sink, void* stream) {
+  if (rows == 0 || rows > (1ull << 36)) return -1;
+  hipLaunchKernelGGL(stream_read, dim3(grid_for(rows, 16)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint8_t*)src, rows, never, (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int bench_stream_write(void* dst, uint64_t rows, int policy, void* stream) {
+  if (rows == 0 || rows > (1ull << 36) || policy < 0 || policy > 2) return -1;
+  const dim3 g(grid_for(rows, 16)), b(256);
+  const hipStream_t s = (hipStream_t)stream;
+  if (policy == 0) hipLaunchKernelGGL(stream_write<0>, g, b, 0, s, (uint8_t*)dst, rows, 0x5A5Au);
+  if (policy == 1) hipLaunchKernelGGL(stream_write<1>, g, b, 0, s, (uint8_t*)dst, rows, 0x5A5Au);
+  if (policy == 2) hipLaunchKernelGGL(stream_write<2>, g, b, 0, s, (uint8_t*)dst, rows, 0x5A5Au);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units, void* stream) {
+  if (units == 0 || units > (1ull << 36)) return -1;
+  hipLaunchKernelGGL(stream_irq, dim3(grid_for(units, 8)), dim3(128), 0, (hipStream_t)stream,
+                     (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int bench_stream_empty(void* stream) {
+  hipLaunchKernelGGL(stream_empty, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // extern "C"

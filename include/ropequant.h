@@ -36,6 +36,11 @@
  *     library never allocates, frees, synchronizes or keeps state; it is
  *     reentrant.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and the call returns without waiting.
+ *   - Launch shape: a fixed table picks the workgroup size from the size of
+ *     the call alone (the analogue of [P4] section 4's program-count rule):
+ *     calls of at least 16384 512-dim units (indexer: 8192 4-head items) use
+ *     128-thread workgroups for inv_rope_fp8_quant and 256 for the others,
+ *     smaller calls 64.  Results never depend on the entry taken.
  *   - Return value: RQ_OK (0) or a negative RQ_ERR_* status.  On any error
  *     nothing is launched and no output byte is touched.  n_tokens == 0
  *     returns RQ_OK with no launch (pointers are then not inspected).
@@ -48,6 +53,13 @@
  *     NaN, its codes being unspecified; qnorm_rope writes such a head as bf16
  *     NaN (0x7FC0); and a slot outside [0, num_blocks * cache_block_size) is
  *     skipped.
+ *   - Finite inputs can still rotate past the fp32 range (a GPT-J or
+ *     rotate-half pair near the bf16 maximum).  The block holding such a
+ *     value gets an infinite maximum and the IEEE results of the usual
+ *     formulas: scale +inf (FP32; its other codes are signed zeros) or
+ *     exponent byte 0xFF, the E8M0 NaN (UE8M0; its finite values scaled by
+ *     2^-128), and for the indexer an infinite q_scale and folded weight.
+ *     The code written for the infinite value itself is unspecified.
  *   - Strides are in elements of the tensor's own type unless "bytes" is said.
  *     Strides that place any element of a tensor more than 2^56 bytes from
  *     its base (or overflow 64-bit arithmetic on the way) return
@@ -65,7 +77,7 @@
 extern "C" {
 #endif
 
-#define ROPEQUANT_ABI_VERSION 2
+#define ROPEQUANT_ABI_VERSION 3
 
 enum {
   RQ_OK = 0,
@@ -303,17 +315,6 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
                          int32_t n_heads, double softmax_scale, double head_scale, double eps,
                          uint8_t* q_fp8, int64_t out_stride_token, int64_t out_stride_head,
                          float* weights_out, int64_t wo_stride_token, void* stream);
-
-/*
- * Launch-shape knob (process-wide, thread-safe): 0 lets the launch table pick
- * the workgroup size from the unit count (for >= 16384 units 128 threads for
- * inv_rope_fp8_quant and 256 for the other calls, else 64: the analogue of
- * [P4] section 4's program-count rule); 64, 128 or
- * 256 forces that size for every later launch.  Results never depend on it;
- * it exists for tuning and for the launch-invariance tests.  Returns RQ_OK
- * or RQ_ERR_VALUE.
- */
-int ropequant_set_block_threads(int threads);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* ropequant_strerror(int status);

@@ -27,7 +27,7 @@ __all__ = [
     "kv_rope_quant_insert", "kv_rope_insert_full", "qnorm_rope_kv_rope_quant_insert",
     "qnorm_rope_kv_rope_insert_full", "qnorm_rope_fp8_kv_rope_insert_full",
     "indexer_q_rope_quant", "empty_inv_rope_fp8_quant_outputs", "empty_qnorm_rope_fp8_outputs",
-    "empty_kv_cache", "set_block_threads", "abi_version", "RopeQuantError", "RECORD_BYTES",
+    "empty_kv_cache", "abi_version", "RopeQuantError", "RECORD_BYTES",
     "SCALE_FMTS",
 ]
 
@@ -97,11 +97,6 @@ def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
 
 def abi_version():
     return lib().ropequant_abi_version()
-
-
-def set_block_threads(threads=0):
-    """Force the workgroup size (64, 128, 256) or restore the table (0)."""
-    check("ropequant_set_block_threads", lib().ropequant_set_block_threads(int(threads)))
 
 
 def empty_inv_rope_fp8_quant_outputs(n_tokens, n_heads, heads_per_group, device,

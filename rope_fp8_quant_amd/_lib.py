@@ -17,8 +17,7 @@ RQ_SCALE_UE8M0 = 1
 EXPORTS = ("inv_rope_fp8_quant", "inv_rope_bf16", "qnorm_rope", "qnorm_rope_fp8",
            "kv_rope_quant_insert", "kv_rope_insert_full", "qnorm_rope_kv_rope_quant_insert",
            "qnorm_rope_kv_rope_insert_full", "qnorm_rope_fp8_kv_rope_insert_full",
-           "indexer_q_rope_quant", "ropequant_strerror", "ropequant_abi_version",
-           "ropequant_set_block_threads")
+           "indexer_q_rope_quant", "ropequant_strerror", "ropequant_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -79,8 +78,6 @@ def lib():
         L.ropequant_strerror.restype = ctypes.c_char_p
         L.ropequant_abi_version.argtypes = []
         L.ropequant_abi_version.restype = I
-        L.ropequant_set_block_threads.argtypes = [I]
-        L.ropequant_set_block_threads.restype = I
         _lib = L
     return _lib
 

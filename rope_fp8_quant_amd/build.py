@@ -25,10 +25,11 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def compile_hip(src: str, out: str, verbose: bool = False) -> str:
+    """hipcc `src` for gfx950 into the shared library `out` with the flags above."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", SRC, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,8 +41,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    return compile_hip(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -8,7 +8,8 @@
 //    FMA residual, for positive normal s below 2^126.
 // Both hold for every input in those domains: tests/exact checks every
 // positive normal fp32 on the host (the first) and on the GPU (both).
-// Callers keep the division's results for an amax that overflowed to +inf.
+// Neither form is used for an amax that overflowed to +inf: the callers
+// take the IEEE results there directly (inf / 448 = inf, 1 / inf = 0).
 #ifndef ROPEQUANT_EXACT_DIV_H
 #define ROPEQUANT_EXACT_DIV_H
 

@@ -42,7 +42,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
-#include <atomic>
 #include <cstring>
 
 #include "ropequant.h"
@@ -122,6 +121,19 @@ template <int CTRL>
 __device__ __forceinline__ float max_dpp_nonneg(float m) {
   const uint32_t u = __builtin_bit_cast(uint32_t, m);
   return __builtin_bit_cast(float, max(u, dpp_u32<CTRL>(u)));
+}
+
+// 2^k and 2^-k for the power-of-two (UE8M0) scales, k in [-126, 128].  A
+// finite amax gives k <= 120 (t = amax / 448 < 2^120); k = 128 comes only
+// from an amax that overflowed to +inf, where 2^k is +inf and 2^-k the
+// subnormal 2^-128, as exact powers of two (so the codes of the block's
+// finite values are still their exact scaling).
+__device__ __forceinline__ float pow2_f32(int k) {
+  return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
+}
+__device__ __forceinline__ float pow2_neg_f32(int k) {
+  return __builtin_bit_cast(float, k < 127 ? (uint32_t)(127 - k) << 23
+                                           : 0x00400000u >> (k - 127));
 }
 
 // The lane's 32 values: x[k][e] is dim lane_dim0 + 32k + e.
@@ -268,8 +280,8 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
     const float t = m < __builtin_inff() ? div448(m) : m;
     const uint32_t u = __builtin_bit_cast(uint32_t, t);
     const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
-    scale = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
-    mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
+    scale = pow2_f32(kexp);
+    mult = pow2_neg_f32(kexp);
     ebyte = (uint32_t)(kexp + 127);
   } else {
     const bool finite = m < __builtin_inff();
@@ -1042,8 +1054,8 @@ __device__ __forceinline__ void idx_items(const IdxParams& p, uint32_t item0, in
     m = __builtin_fmaxf(m, p.eps);
     const uint32_t tb = __builtin_bit_cast(uint32_t, m < __builtin_inff() ? div448(m) : m);
     const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
-    const float qs = __builtin_bit_cast(float, (uint32_t)(kexp + 127) << 23);
-    const float mult = __builtin_bit_cast(float, (uint32_t)(127 - kexp) << 23);
+    const float qs = pow2_f32(kexp);
+    const float mult = pow2_neg_f32(kexp);
     uint32_t code[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1073,8 +1085,6 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
 
 // ------------------------------------------------------------ host side
 
-std::atomic<int> g_block_threads{0};  // 0: launch table decides
-
 Magic make_magic(uint32_t d) {
   uint32_t s = 0;
   while ((1ull << s) < d) ++s;
@@ -1095,8 +1105,6 @@ struct LaunchShape {
 // workgroups (4 units) so the work spreads over as many CUs as possible.
 // Results do not depend on the choice.
 int pick_block_threads(uint32_t units, int prefill_threads) {
-  const int forced = g_block_threads.load(std::memory_order_relaxed);
-  if (forced) return forced;
   return units >= 16384u ? prefill_threads : 64;
 }
 
@@ -1196,12 +1204,6 @@ const char* ropequant_strerror(int status) {
     case RQ_ERR_HIP: return "the HIP runtime refused the launch";
     default: return "unknown status";
   }
-}
-
-int ropequant_set_block_threads(int threads) {
-  if (threads != 0 && threads != 64 && threads != 128 && threads != 256) return RQ_ERR_VALUE;
-  g_block_threads.store(threads, std::memory_order_relaxed);
-  return RQ_OK;
 }
 
 int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,

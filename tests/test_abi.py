@@ -55,11 +55,14 @@ def test_status_strings_distinct():
     assert L.ropequant_strerror(-99).decode() == "unknown status"
 
 
-def test_block_threads_knob():
-    L = _lib.lib()
-    assert L.ropequant_set_block_threads(100) == VALUE
-    for t in (64, 128, 256, 0):
-        assert L.ropequant_set_block_threads(t) == OK
+def test_exports_are_exactly_the_declared_functions():
+    # nothing beyond the header: in particular no process-wide setting that
+    # one caller could change under another
+    syms = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    exported = {line.split()[-1] for line in syms.splitlines() if line.split()[1:2] == ["T"]}
+    assert exported == set(declared_functions())
+    assert set(_lib.EXPORTS) == exported
 
 
 A = 0x100000  # fake, 256-byte aligned "device" addresses

@@ -6,18 +6,12 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, SHAPES, assert_bits_equal, assert_codes_match, dev, host,
+                            table_tokens)
 
 pytestmark = pytest.mark.gpu
 
 SOFTMAX_SCALE = 128 ** -0.5
-
-
-@pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
-    yield
-    rq.set_block_threads(0)
 
 
 def idx_inputs(N, H, seed, max_pos=4096, pos=None):
@@ -53,10 +47,11 @@ def test_indexer_full_size():
               "4096x64x128")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_indexer_ragged(threads):
-    rq.set_block_threads(threads)
-    idx_check(*idx_inputs(37, 5, 56, max_pos=65536), f"ragged threads={threads}")
+# A wave takes two 4-head items, so a token of H heads is 2 * ceil(H / 4)
+# rows of the launch table.
+@pytest.mark.parametrize("shape", SHAPES)
+def test_indexer_ragged(shape):
+    idx_check(*idx_inputs(table_tokens(shape, 4), 5, 56, max_pos=65536), f"ragged {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -75,19 +70,18 @@ def test_indexer_strided_input_and_in_place_weights():
     assert_codes_match(got, exp, "strided codes")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_indexer_strided_outputs_partial_item(threads):
+@pytest.mark.parametrize("shape", SHAPES)
+def test_indexer_strided_outputs_partial_item(shape):
     # 7 heads: every token's second 4-head item holds 3 heads.  Codes rows
     # padded to 192 bytes, weight rows to 10 and 12 floats; the padding must
     # come back untouched.
-    rq.set_block_threads(threads)
-    N, H = 41, 7
+    N, H = table_tokens(shape, 4, base=41), 7
     q, w, pos, cache = idx_inputs(N, H, 62, max_pos=65536)
     q8_big = torch.full((N, H, 192), 0xCD, dtype=torch.uint8, device=DEV)
     w_big = torch.full((N, 10), -7.0, dtype=torch.float32, device=DEV)
     w_big[:, :H] = dev(w)
     wo_big = torch.full((N, 12), -3.0, dtype=torch.float32, device=DEV)
-    print(f"[case] indexer strided outputs threads={threads}", flush=True)
+    print(f"[case] indexer strided outputs {shape}", flush=True)
     rq.indexer_q_rope_quant(dev(q), dev(pos), dev(cache), w_big[:, :H], q8_big[:, :, :128],
                             wo_big[:, :H], SOFTMAX_SCALE, 0.5)
     torch.cuda.synchronize()
@@ -115,6 +109,31 @@ def test_indexer_degenerate_heads():
         idx_check(q, w, pos, synth.cos_sin_cache(4096), f"degenerate eps={eps}", eps=eps)
 
 
+def test_indexer_rotated_pair_near_and_past_overflow():
+    # Rotate-half pair (i, i+32) = (v, -v) at 45 degrees: r0 = (v + v) * 0.7071.
+    # v = 1.5 * 2^126 stays finite; v = the bf16 maximum overflows, so the
+    # head's maximum is +inf: q_scale 2^128 = inf, folded weight +inf, finite
+    # values scaled by 2^-128.  Weights and every code but the infinite
+    # value's (unspecified) must match the oracle.
+    N, H = 4, 8
+    q, w, _, _ = idx_inputs(N, H, 63)
+    pos = np.array([1, 0, 1, 1], np.int64)
+    cache = np.zeros((2, 64), np.float32)
+    cache[0, :32] = 1.0
+    cache[1, :] = np.float32(np.sqrt(0.5))
+    q[0, 2, 5], q[0, 2, 37] = 0x7EC0, 0xFEC0   # 1.5 * 2^126, negated
+    q[2, 6, 9], q[2, 6, 41] = 0x7F7F, 0xFF7F   # the bf16 maximum, negated
+    q[3, 1, 0], q[3, 1, 32] = 0x7F7F, 0xFF7F
+    print("[case] indexer rotated overflow", flush=True)
+    got, gw = idx_gpu(q, w, pos, cache)
+    exp, ew = oracle.indexer_q_rope_quant(q, pos, cache, w, SOFTMAX_SCALE)
+    assert_bits_equal(gw, ew, "overflow weights")
+    assert np.isinf(ew[2, 6]) and np.isinf(ew[3, 1]) and np.isfinite(ew[0, 2])
+    keep = np.ones(exp.shape, bool)
+    keep[2, 6, 9] = keep[3, 1, 0] = False  # the infinite values
+    assert_codes_match(got[keep], exp[keep], "overflow codes")
+
+
 def test_indexer_bad_position_gives_nan_weight():
     q, w, pos, cache = idx_inputs(6, 4, 59)
     bad = pos.copy()
@@ -127,11 +146,14 @@ def test_indexer_bad_position_gives_nan_weight():
     assert np.isnan(gw[3]).all()
 
 
-def test_indexer_launch_shapes_bit_identical():
-    q, w, pos, cache = idx_inputs(301, 64, 61, max_pos=65536)
-    res = []
-    for threads in (64, 128, 256):
-        rq.set_block_threads(threads)
-        res.append(idx_gpu(q, w, pos, cache))
-    for got, gw in res[1:]:
-        assert (got == res[0][0]).all() and (gw.view(np.uint32) == res[0][1].view(np.uint32)).all()
+def test_indexer_launch_table_entries_bit_identical():
+    # 613 tokens x 64 heads (32 rows each) take the prefill entry of the
+    # launch table; the same tokens in two calls of under 512 tokens take the
+    # 64-thread entry
+    q, w, pos, cache = idx_inputs(613, 64, 61, max_pos=65536)
+    print("[case] indexer launch-table entries", flush=True)
+    full, fw = idx_gpu(q, w, pos, cache)
+    for t0, t1 in ((0, 307), (307, 613)):
+        part, pw = idx_gpu(q[t0:t1].copy(), w[t0:t1].copy(), pos[t0:t1].copy(), cache)
+        assert (part == full[t0:t1]).all()
+        assert (pw.view(np.uint32) == fw[t0:t1].view(np.uint32)).all()

@@ -6,18 +6,12 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, SHAPES, assert_bits_equal, assert_codes_match, dev, host,
+                            table_tokens)
 
 pytestmark = pytest.mark.gpu
 
 FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
-
-
-@pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
-    yield
-    rq.set_block_threads(0)
 
 
 def run_gpu(o_bits, pos, cache, hpg, scale_fmt="fp32", eps=1e-10):
@@ -46,15 +40,15 @@ def test_irq_tiny(scale_fmt):
     check(o, pos, cache, 8, scale_fmt, what="tiny")
 
 
-# The pages' (heads, groups) grid, plus 48 heads in groups of 6; N = 37 leaves a
-# ragged tail in every launch shape.
+# The pages' (heads, groups) grid, plus 48 heads in groups of 6, at a size in
+# each entry of the launch table.
 @pytest.mark.parametrize("H,G", [(64, 8), (32, 4), (128, 8), (24, 4), (48, 8)])
-@pytest.mark.parametrize("threads", [64, 256])
-def test_irq_head_group_grid(H, G, threads):
-    rq.set_block_threads(threads)
-    cfg = dict(synth.IRQ_TINY, N=37, H=H, hpg=H // G, max_pos=65536, seed=H * 10 + G)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_irq_head_group_grid(H, G, shape):
+    N = table_tokens(shape, H)
+    cfg = dict(synth.IRQ_TINY, N=N, H=H, hpg=H // G, max_pos=65536, seed=H * 10 + G)
     o, pos, cache = synth.irq_inputs(cfg)
-    check(o, pos, cache, H // G, what=f"grid threads={threads}")
+    check(o, pos, cache, H // G, what=f"grid {shape}")
 
 
 def test_irq_prefill_full_size():
@@ -79,15 +73,18 @@ def test_irq_decode_sizes(N):
     check(o, pos, cache, 8, what="decode")
 
 
-def test_irq_launch_shapes_bit_identical():
-    cfg = dict(synth.IRQ_TINY, N=301, H=32, hpg=8, max_pos=65536, seed=77)
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_irq_launch_table_entries_bit_identical(scale_fmt):
+    # 613 tokens x 32 heads take the prefill entry of the launch table; the
+    # same tokens in two calls of under 512 tokens take the 64-thread entry
+    cfg = dict(synth.IRQ_TINY, N=613, H=32, hpg=8, max_pos=65536, seed=77)
     o, pos, cache = synth.irq_inputs(cfg)
-    res = []
-    for threads in (64, 128, 256):
-        rq.set_block_threads(threads)
-        res.append(run_gpu(o, pos, cache, 8))
-    for out, sc in res[1:]:
-        assert (out == res[0][0]).all() and (sc.view(np.uint32) == res[0][1].view(np.uint32)).all()
+    print(f"[case] irq launch-table entries {scale_fmt}", flush=True)
+    full, fsc = run_gpu(o, pos, cache, 8, scale_fmt)
+    for t0, t1 in ((0, 307), (307, 613)):
+        part, psc = run_gpu(o[t0:t1].copy(), pos[t0:t1].copy(), cache, 8, scale_fmt)
+        assert (part == full[:, t0:t1]).all()
+        assert (psc.view(np.uint32) == fsc[:, t0:t1].view(np.uint32)).all()
 
 
 def test_irq_batch_invariance():
@@ -202,6 +199,47 @@ def test_irq_bad_position_poisons_only_its_token(scale_fmt):
             assert np.isnan(sc[:, t]).all()
         else:
             assert (sc[:, t] == 0xFFFFFFFF).all()
+
+
+def _half_turn_cache():
+    """Row 0: cos 1, sin 0.  Row 1: cos = sin = fp32(sqrt(1/2)) in every column."""
+    cache = np.zeros((2, 64), np.float32)
+    cache[0, :32] = 1.0
+    cache[1, :] = np.float32(np.sqrt(0.5))
+    return cache
+
+
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_irq_rotated_pair_near_and_past_overflow(scale_fmt):
+    # The last GPT-J pair (dims 510, 511) of some heads is set to (v, v) and
+    # rotated by 45 degrees: e' = (e + o) * 0.7071.  v = 1.5 * 2^126 stays
+    # finite (1.06 * 2^127); v = the bf16 maximum overflows to +inf, giving
+    # block 3 an infinite maximum (scale +inf, or UE8M0 byte 0xFF).  Scales
+    # must match the oracle bit for bit, and every code but the infinite
+    # value's (unspecified) to the code bar.
+    N, H, hpg = 8, 8, 4
+    G = H // hpg
+    o = synth.normal_bf16((N, H, 512), 83, synth.T_O)
+    pos = np.array([0, 1, 1, 0, 1, 1, 1, 0], np.int64)
+    near = [(1, 0), (2, 5), (4, 7)]
+    past = [(1, 3), (5, 0), (6, 6)]
+    for t, h in near:
+        o[t, h, 510:512] = 0x7EC0  # 1.5 * 2^126
+    for t, h in past:
+        o[t, h, 510:512] = 0x7F7F  # the largest finite bf16
+    cache = _half_turn_cache()
+    print(f"[case] irq rotated overflow fmt={scale_fmt}", flush=True)
+    out, sc = run_gpu(o, pos, cache, hpg, scale_fmt)
+    eo, es = oracle.inv_rope_fp8_quant(o, pos, cache, hpg, FMT[scale_fmt])
+    assert_bits_equal(sc, es, "overflow scales")
+    if scale_fmt == "fp32":
+        assert all(np.isinf(es[h // hpg, t, (h % hpg) * 4 + 3]) for t, h in past)
+    else:
+        assert all(es[h // hpg, t, h % hpg] >> 24 == 0xFF for t, h in past)
+    keep = np.ones(eo.shape, bool)
+    for t, h in past:
+        keep[h // hpg, t, (h % hpg) * 512 + 510] = False  # the infinite value
+    assert_codes_match(out[keep], eo[keep], "overflow codes")
 
 
 def test_irq_zero_tokens_is_a_no_op():

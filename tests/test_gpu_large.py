@@ -14,7 +14,8 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, assert_bits_equal, assert_codes_match, assert_q_out_parity,
+                            dev, host)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,10 +23,8 @@ BLOCK = 1024  # tokens in the repeated block
 
 
 @pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
+def _release_memory():
     yield
-    rq.set_block_threads(0)
     torch.cuda.empty_cache()
 
 
@@ -83,8 +82,8 @@ def test_qnr_past_4_gib():
     del q
     ts = sample_tokens(N, Hpad * 1024, 74)
     got = host(q_out.index_select(0, torch.from_numpy(ts).to(DEV)))
-    exp = oracle.qnorm_rope(small[ts % BLOCK], w, pos[ts], cache, Hpad, cfg["eps"])
-    assert_bits_equal(got, exp, "large qnorm_rope")
+    assert_q_out_parity(got, small[ts % BLOCK], w, pos[ts], cache, Hpad, cfg["eps"],
+                        "large qnorm_rope")
 
 
 def test_kvi_past_4_gib():

@@ -7,18 +7,12 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, SHAPES, assert_bits_equal, assert_codes_match,
+                            assert_q_out_parity, dev, host, table_tokens)
 
 pytestmark = pytest.mark.gpu
 
 FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
-
-
-@pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
-    yield
-    rq.set_block_threads(0)
 
 
 # ------------------------------------------------------------- qnorm_rope
@@ -36,9 +30,8 @@ def qnr_gpu(q, w, pos, cache, hpad, eps, q_dev=None):
 def qnr_check(q, w, pos, cache, hpad, eps, what, q_dev=None):
     print(f"[case] qnr {what} N={q.shape[0]} Hq={q.shape[1]} Hpad={hpad}", flush=True)
     got = qnr_gpu(q, w, pos, cache, hpad, eps, q_dev)
-    exp = oracle.qnorm_rope(q, w, pos, cache, hpad, eps)
     assert (got[:, q.shape[1]:] == 0).all(), "pad heads not zero"
-    assert_bits_equal(got, exp, f"qnr {what}")
+    assert_q_out_parity(got, q, w, pos, cache, hpad, eps, f"qnr {what}")
     return got
 
 
@@ -48,12 +41,12 @@ def test_qnr_forward_full_size():
     qnr_check(q, w, pos, cache, cfg["Hpad"], cfg["eps"], "forward 8192x64->128")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_qnr_ragged_no_weight(threads):
-    rq.set_block_threads(threads)
-    cfg = dict(synth.QNR_FORWARD, N=37, Hq=5, Hpad=7, max_pos=65536, seed=31)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_qnr_ragged_no_weight(shape):
+    cfg = dict(synth.QNR_FORWARD, N=table_tokens(shape, 7), Hq=5, Hpad=7, max_pos=65536,
+               seed=31)
     q, _, pos, cache = synth.qnr_inputs(cfg)
-    qnr_check(q, None, pos, cache, 7, 1e-6, f"ragged no-weight threads={threads}")
+    qnr_check(q, None, pos, cache, 7, 1e-6, f"ragged no-weight {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -93,8 +86,8 @@ def test_qnr_bad_position_poisons_only_its_token():
     bad[2] = -5
     got = qnr_gpu(q, w, bad, cache, 4, 1e-6)
     good = [0, 1, 3, 4, 5]
-    exp = oracle.qnorm_rope(q[good].copy(), w, pos[good].copy(), cache, 4, 1e-6)
-    assert (got[good] == exp).all()
+    assert_q_out_parity(got[good], q[good].copy(), w, pos[good].copy(), cache, 4, 1e-6,
+                        "good tokens")
     assert (got[2, :3] == 0x7FC0).all() and (got[2, 3] == 0).all()
 
 
@@ -136,10 +129,10 @@ def test_kvi_forward_full_size(scale_fmt):
               "forward 8192 -> 256x64")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_kvi_holes_gaps_and_out_of_range(threads):
-    rq.set_block_threads(threads)
-    N, nb, bs = 45, 5, 16
+@pytest.mark.parametrize("shape", SHAPES)
+def test_kvi_holes_gaps_and_out_of_range(shape):
+    N, bs = table_tokens(shape, 1, base=45), 16
+    nb = -(-N // bs) + 2
     kv = synth.normal_bf16((N, 512), 35, synth.T_KV)
     pos = synth.uniform_positions(N, 65536, 35)
     slots = synth.slot_permutation(N, nb * bs, 35)
@@ -148,7 +141,7 @@ def test_kvi_holes_gaps_and_out_of_range(threads):
     o_slots = slots.copy()
     o_slots[[7, 20]] = -1
     kvi_check(kv, pos, synth.cos_sin_cache(65536), slots, nb, bs, bs * 528 + 64, "fp32",
-              f"holes threads={threads}", oracle_slots=o_slots)
+              f"holes {shape}", oracle_slots=o_slots)
 
 
 def test_kvi_bad_position_poisons_its_record():

@@ -1,9 +1,10 @@
 """Seeded random sweeps of every op against the oracle, and stream ordering.
 
 Each case draws its shape, grouping, strides (padded rows), scale format,
-positions, slot holes and launch shape from a seeded generator, runs the HIP
-path through the C ABI and compares with the oracle to the parity bar.  The
-case parameters are printed before each GPU step.
+positions and slot holes from a seeded generator, at a size in one of the
+two entries of the launch table, runs the HIP path through the C ABI and
+compares with the oracle to the parity bar.  The case parameters are printed
+before each GPU step.
 """
 import numpy as np
 import pytest
@@ -12,20 +13,21 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, SHAPES, TABLE_ROWS, assert_bits_equal, assert_codes_match,
+                            assert_q_fp8_parity, assert_q_out_parity, dev, host)
 
 pytestmark = pytest.mark.gpu
 
 FMTS = ("fp32", "ue8m0")
 FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
-THREADS = (0, 64, 128, 256)
 
 
-@pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
-    yield
-    rq.set_block_threads(0)
+def draw_tokens(rng, shape, rows_per_token, spread):
+    """A token count whose launch of rows_per_token 16-lane rows per token
+    lands in table entry `shape`."""
+    if shape == SHAPES[0]:
+        return int(rng.integers(1, min(spread, (TABLE_ROWS - 1) // rows_per_token) + 1))
+    return -(-TABLE_ROWS // rows_per_token) + int(rng.integers(0, spread))
 
 
 def padded(a, pad_elems, seed):
@@ -46,14 +48,13 @@ def test_irq_random(case):
     rng = np.random.default_rng([200, case])
     hpg = int(rng.choice([1, 2, 3, 4, 6, 8, 12]))
     G = int(rng.integers(1, 6))
-    N = int(rng.integers(1, 300))
+    shape = SHAPES[(case // 2) % 2]
+    N = draw_tokens(rng, shape, G * hpg, 300)
     fmt = FMTS[case % 2]
-    thr = THREADS[case % 4]
     pad = int(rng.choice([0, 8, 64]))
     max_pos = int(rng.choice([64, 4096, 65536]))
-    print(f"[case] irq random #{case}: N={N} H={G * hpg} hpg={hpg} fmt={fmt} threads={thr} "
+    print(f"[case] irq random #{case}: N={N} H={G * hpg} hpg={hpg} fmt={fmt} {shape} "
           f"pad={pad} max_pos={max_pos}", flush=True)
-    rq.set_block_threads(thr)
     o = synth.normal_bf16((N, G * hpg, 512), 210 + case, synth.T_O, outlier_frac=0.01)
     pos = rng.integers(0, max_pos, N).astype(np.int64)
     cache = synth.cos_sin_cache(max_pos)
@@ -73,17 +74,16 @@ def test_irq_random(case):
 @pytest.mark.parametrize("case", range(10))
 def test_q_paths_random(case):
     rng = np.random.default_rng([300, case])
-    N = int(rng.integers(1, 200))
     Hq = int(rng.integers(1, 20))
     Hpad = Hq + int(rng.choice([0, 1, 3, 8, 20]))
-    thr = THREADS[case % 4]
+    shape = SHAPES[(case // 2) % 2]
+    N = draw_tokens(rng, shape, Hpad, 200)
     fmt = FMTS[case % 2]
     pad = int(rng.choice([0, 8, 136]))
     weighted = bool(case % 3)
     eps = float(rng.choice([1e-6, 1e-3, 0.5]))
-    print(f"[case] q paths random #{case}: N={N} Hq={Hq} Hpad={Hpad} fmt={fmt} threads={thr} "
+    print(f"[case] q paths random #{case}: N={N} Hq={Hq} Hpad={Hpad} fmt={fmt} {shape} "
           f"pad={pad} weight={weighted} eps={eps}", flush=True)
-    rq.set_block_threads(thr)
     q = synth.normal_bf16((N, Hq, 512), 310 + case, synth.T_Q, std=float(rng.uniform(0.1, 4)))
     w = synth.uniform_bf16((512,), 310 + case, synth.T_W, 0.5, 1.5) if weighted else None
     pos = rng.integers(0, 65536, N).astype(np.int64)
@@ -95,25 +95,22 @@ def test_q_paths_random(case):
     codes, sc = rq.empty_qnorm_rope_fp8_outputs(N, Hpad, DEV, fmt)
     rq.qnorm_rope_fp8(qd, wd, dev(pos), dev(cache), codes, sc, eps, fmt)
     torch.cuda.synchronize()
-    assert_bits_equal(host(q_out), oracle.qnorm_rope(q, w, pos, cache, Hpad, eps), "random qnr")
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, Hpad, eps, FMT[fmt])
-    assert_bits_equal(host(sc), es, "random qf8 scales")
-    assert_codes_match(host(codes), ec, "random qf8 codes")
+    assert_q_out_parity(host(q_out), q, w, pos, cache, Hpad, eps, "random qnr")
+    assert_q_fp8_parity(host(codes), host(sc), q, w, pos, cache, Hpad, eps, fmt, "random qf8")
 
 
 @pytest.mark.parametrize("case", range(10))
 def test_kv_paths_random(case):
     rng = np.random.default_rng([400, case])
-    N = int(rng.integers(1, 400))
+    shape = SHAPES[(case // 2) % 2]
+    N = draw_tokens(rng, shape, 1, 400)
     bs = int(rng.choice([1, 4, 16, 64]))
     nb = -(-(N + int(rng.integers(0, 50))) // bs)
     fmt = FMTS[case % 2]
-    thr = THREADS[case % 4]
     gap = int(rng.choice([0, 16, 528]))
     pad = int(rng.choice([0, 8]))
-    print(f"[case] kv paths random #{case}: N={N} blocks={nb}x{bs} fmt={fmt} threads={thr} "
+    print(f"[case] kv paths random #{case}: N={N} blocks={nb}x{bs} fmt={fmt} {shape} "
           f"gap={gap} pad={pad}", flush=True)
-    rq.set_block_threads(thr)
     kv = synth.normal_bf16((N, 512), 410 + case, synth.T_KV)
     pos = rng.integers(0, 4096, N).astype(np.int64)
     slots = synth.slot_permutation(N, nb * bs, 410 + case)
@@ -146,13 +143,13 @@ def test_kv_paths_random(case):
 @pytest.mark.parametrize("case", range(8))
 def test_indexer_random(case):
     rng = np.random.default_rng([500, case])
-    N = int(rng.integers(1, 300))
     H = int(rng.integers(1, 70))
-    thr = THREADS[case % 4]
+    shape = SHAPES[case % 2]
+    # four rows per wave of two 4-head items: 2 * ceil(H / 4) rows per token
+    N = draw_tokens(rng, shape, 2 * (-(-H // 4)), 300)
     hs = float(rng.uniform(0.25, 2.0))
-    print(f"[case] indexer random #{case}: N={N} H={H} threads={thr} head_scale={hs:.3f}",
+    print(f"[case] indexer random #{case}: N={N} H={H} {shape} head_scale={hs:.3f}",
           flush=True)
-    rq.set_block_threads(thr)
     q = synth.normal_bf16((N, H, 128), 510 + case, synth.T_Q, std=float(rng.uniform(0.01, 30)))
     w = rng.uniform(0, 1, (N, H)).astype(np.float32)
     pos = rng.integers(0, 65536, N).astype(np.int64)
@@ -172,16 +169,16 @@ def test_fused_forms_random(case):
     # and kv work in neighbouring waves.  Each fused form must equal its two
     # separate calls bit for bit, and the oracle.
     rng = np.random.default_rng([700, case])
-    N = int(rng.integers(1, 150))
     Hq = int(rng.integers(1, 11))
     Hpad = Hq + int(rng.choice([0, 1, 2, 5]))
     form = ("quant", "full_fp8", "full_bf16")[case % 3]
     fmt = FMTS[(case // 3) % 2]
-    thr = THREADS[case % 4]
+    shape = SHAPES[case % 2]
+    # one grid: a q row per head (Hq in place, else Hpad) and one kv row per token
+    N = draw_tokens(rng, shape, (Hq if form == "full_bf16" else Hpad) + 1, 150)
     weighted = case % 2 == 0
     print(f"[case] fused random #{case}: form={form} N={N} Hq={Hq} Hpad={Hpad} fmt={fmt} "
-          f"threads={thr} weight={weighted}", flush=True)
-    rq.set_block_threads(thr)
+          f"{shape} weight={weighted}", flush=True)
     q = synth.normal_bf16((N, Hq, 512), 710 + case, synth.T_Q, std=2.0)
     w = synth.uniform_bf16((512,), 710 + case, synth.T_W, 0.5, 1.5) if weighted else None
     kv = synth.normal_bf16((N, 512), 710 + case, synth.T_KV)
@@ -206,10 +203,10 @@ def test_fused_forms_random(case):
             outs.append((host(q_out), host(k_cache)))
         assert_bits_equal(outs[0][0], outs[1][0], "fused vs separate q_out")
         assert_bits_equal(outs[0][1], outs[1][1], "fused vs separate k_cache")
-        eq, ek = oracle.qnorm_rope_kv_rope_quant_insert(
-            q, w, kv, pos, cache, slots, np.full((nb, bs * 528), 0xAA, np.uint8), Hpad, bs,
-            1e-6, FMT[fmt])
-        assert_bits_equal(outs[0][0], eq, "fused q_out vs oracle")
+        assert_q_out_parity(outs[0][0], q, w, pos, cache, Hpad, 1e-6, "fused q_out vs oracle")
+        ek = oracle.kv_rope_quant_insert(kv, pos, cache, slots,
+                                         np.full((nb, bs * 528), 0xAA, np.uint8), bs,
+                                         scale_fmt=FMT[fmt])
         rec = np.zeros(ek.size, bool)
         for s_ in slots[slots >= 0]:
             rec[(s_ // bs) * bs * 528 + (s_ % bs) * 528:][:512] = True
@@ -249,12 +246,10 @@ def test_fused_forms_random(case):
     ef = oracle.kv_rope_insert_full(kv, pos, cache, slots, np.full((ns, 512), 0xAAAA, np.uint16))
     assert_bits_equal(full[0][2], ef, "fused kv cache vs oracle")
     if form == "full_fp8":
-        ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, Hpad, 1e-6, FMT[fmt])
-        assert_bits_equal(full[0][1], es, "fused q scales vs oracle")
-        assert_codes_match(full[0][0], ec, "fused q codes vs oracle")
+        assert_q_fp8_parity(full[0][0], full[0][1], q, w, pos, cache, Hpad, 1e-6, fmt,
+                            "fused q vs oracle")
     else:
-        assert_bits_equal(full[0][0], oracle.qnorm_rope(q, w, pos, cache, hp, 1e-6),
-                          "fused in-place q vs oracle")
+        assert_q_out_parity(full[0][0], q, w, pos, cache, hp, 1e-6, "fused in-place q vs oracle")
 
 
 def test_calls_run_in_order_on_the_callers_stream():

@@ -9,18 +9,12 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import DEV, assert_bits_equal, assert_codes_match, dev, host
+from tests.gpu_util import (DEV, SHAPES, assert_bits_equal, assert_codes_match,
+                            assert_q_fp8_parity, assert_q_out_parity, dev, host, table_tokens)
 
 pytestmark = pytest.mark.gpu
 
 FMT = {"fp32": oracle.SCALE_FP32, "ue8m0": oracle.SCALE_UE8M0}
-
-
-@pytest.fixture(autouse=True)
-def _table_launch():
-    rq.set_block_threads(0)
-    yield
-    rq.set_block_threads(0)
 
 
 # ------------------------------------------------------------ inv_rope_bf16
@@ -56,13 +50,13 @@ def test_irb_irregular_full_size_token_major():
     irb_check(o, pos, cache, 6, "irregular 4096x48", layout="token")
 
 
-@pytest.mark.parametrize("H,G", [(64, 8), (24, 4), (48, 8)])
-@pytest.mark.parametrize("threads", [64, 256])
-def test_irb_ragged(H, G, threads):
-    rq.set_block_threads(threads)
-    cfg = dict(synth.IRQ_TINY, N=37, H=H, hpg=H // G, max_pos=65536, seed=H * 7 + G)
+@pytest.mark.parametrize("H,G", [(64, 8), (24, 4), (48, 8), (18, 3)])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_irb_ragged(H, G, shape):
+    cfg = dict(synth.IRQ_TINY, N=table_tokens(shape, H), H=H, hpg=H // G, max_pos=65536,
+               seed=H * 7 + G)
     o, pos, cache = synth.irq_inputs(cfg)
-    irb_check(o, pos, cache, H // G, f"ragged threads={threads}")
+    irb_check(o, pos, cache, H // G, f"ragged {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -132,9 +126,7 @@ def qf8_check(q, w, pos, cache, hpad, scale_fmt, what, **kw):
     print(f"[case] qnorm_rope_fp8 {what} N={q.shape[0]} Hq={q.shape[1]} Hpad={hpad} "
           f"fmt={scale_fmt}", flush=True)
     gc, gs = qf8_gpu(q, w, pos, cache, hpad, scale_fmt, **kw)
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, hpad, 1e-6, FMT[scale_fmt])
-    assert_bits_equal(gs, es, f"qf8 {what} scales")
-    assert_codes_match(gc, ec, f"qf8 {what} codes")
+    assert_q_fp8_parity(gc, gs, q, w, pos, cache, hpad, 1e-6, scale_fmt, f"qf8 {what}")
 
 
 def test_qf8_forward_full_size():
@@ -148,12 +140,11 @@ def test_qf8_forward_ue8m0_token_slice():
 
 
 @pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
-@pytest.mark.parametrize("threads", [64, 256])
-def test_qf8_ragged_no_weight(scale_fmt, threads):
-    rq.set_block_threads(threads)
-    cfg = dict(synth.QNR_FORWARD, N=37, Hq=5, Hpad=7, seed=98)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_qf8_ragged_no_weight(scale_fmt, shape):
+    cfg = dict(synth.QNR_FORWARD, N=table_tokens(shape, 7), Hq=5, Hpad=7, seed=98)
     q, _, pos, cache = synth.qnr_inputs(cfg)
-    qf8_check(q, None, pos, cache, 7, scale_fmt, f"ragged threads={threads}")
+    qf8_check(q, None, pos, cache, 7, scale_fmt, f"ragged {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -175,9 +166,8 @@ def test_qf8_pad_only_waves_take_the_zero_head_scales(scale_fmt, quant_eps):
     rq.qnorm_rope_fp8(dev(q), dev(w), dev(pos), dev(cache), codes, sc, 1e-6, scale_fmt,
                       quant_eps)
     torch.cuda.synchronize()
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, 12, 1e-6, FMT[scale_fmt], quant_eps)
-    assert_bits_equal(host(sc), es, "pad-wave scales")
-    assert_codes_match(host(codes), ec, "pad-wave codes")
+    assert_q_fp8_parity(host(codes), host(sc), q, w, pos, cache, 12, 1e-6, scale_fmt,
+                        "pad waves", quant_eps)
 
 
 def test_qf8_strided_input():
@@ -194,10 +184,10 @@ def test_qf8_bad_position_poisons_live_heads_only():
     bad = pos.copy()
     bad[1] = -3
     gc, gs = qf8_gpu(q, w, bad, cache, 4)
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, 4, 1e-6)
+    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, 4, 1e-6)  # its pad head, below
     good = [0, 2, 3, 4]
-    assert (gc[good] == ec[good]).all() and (gs[good].view(np.uint32) ==
-                                             es[good].view(np.uint32)).all()
+    assert_q_fp8_parity(gc[good], gs[good], q[good].copy(), w, pos[good].copy(), cache, 4, 1e-6,
+                        "fp32", "good tokens")
     assert np.isnan(gs[1, :3]).all()
     assert (gs[1, 3].view(np.uint32) == es[1, 3].view(np.uint32)).all() and (gc[1, 3] == 0).all()
 
@@ -227,10 +217,10 @@ def test_kvf_forward_full_size():
     kvf_check(kv, pos, slots, synth.cos_sin_cache(8192), 256 * 64, 512, "forward 8192")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_kvf_ragged_holes_gap_rows(threads):
-    rq.set_block_threads(threads)
-    kvf_check(*kvf_inputs(37, 50, 122, holes=(0, 11, 36)), 50, 576, f"ragged threads={threads}")
+@pytest.mark.parametrize("shape", SHAPES)
+def test_kvf_ragged_holes_gap_rows(shape):
+    N = table_tokens(shape, 1)
+    kvf_check(*kvf_inputs(N, N + 13, 122, holes=(0, 11, 36)), N + 13, 576, f"ragged {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -264,10 +254,8 @@ def fused_full_inputs(N, Hq, ns, seed, holes=()):
     return q, w, kv, pos, slots, cache
 
 
-@pytest.mark.parametrize("N,Hq,hpad,threads", [(8192, 64, 64, 0), (37, 5, 5, 64),
-                                               (3, 32, 32, 0)])
-def test_fused_full_bf16_in_place(N, Hq, hpad, threads):
-    rq.set_block_threads(threads)
+@pytest.mark.parametrize("N,Hq,hpad", [(8192, 64, 64), (37, 5, 5), (3, 32, 32)])
+def test_fused_full_bf16_in_place(N, Hq, hpad):
     ns = max(2 * N, 64)
     q, w, kv, pos, slots, cache = fused_full_inputs(N, Hq, ns, 130 + N, holes=(1,))
     print(f"[case] fused full bf16 in place N={N} Hq={Hq}", flush=True)
@@ -276,7 +264,7 @@ def test_fused_full_bf16_in_place(N, Hq, hpad, threads):
     rq.qnorm_rope_kv_rope_insert_full(qd, dev(w), dev(kv), dev(pos), dev(cache), dev(slots),
                                       qd, full)
     torch.cuda.synchronize()
-    assert_bits_equal(host(qd), oracle.qnorm_rope(q, w, pos, cache, hpad, 1e-6), "fused q")
+    assert_q_out_parity(host(qd), q, w, pos, cache, hpad, 1e-6, "fused q")
     exp = oracle.kv_rope_insert_full(kv, pos, cache, slots, np.full((ns, 512), 0xAAAA, np.uint16))
     assert_bits_equal(host(full), exp, "fused kv")
 
@@ -303,9 +291,8 @@ def test_fused_full_fp8_matches_oracle_and_separate_calls(scale_fmt, N, Hq, hpad
         res.append((host(codes), host(sc), host(full)))
     for a, b in zip(*res):
         assert (a.view(np.uint8) == b.view(np.uint8)).all(), "fused differs from separate calls"
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, hpad, 1e-6, FMT[scale_fmt])
-    assert_bits_equal(res[0][1], es, "fused fp8 scales")
-    assert_codes_match(res[0][0], ec, "fused fp8 codes")
+    assert_q_fp8_parity(res[0][0], res[0][1], q, w, pos, cache, hpad, 1e-6, scale_fmt,
+                        "fused fp8")
     exp = oracle.kv_rope_insert_full(kv, pos, cache, slots, np.full((ns, 512), 0xAAAA, np.uint16))
     assert_bits_equal(res[0][2], exp, "fused fp8 kv rows")
 
@@ -375,15 +362,14 @@ def test_graph_replays_of_the_other_entry_points_match_eager():
     assert_bits_equal(eager["kvf"], exp, "graph kvf")
 
 
-@pytest.mark.parametrize("threads", [64, 256])
-def test_irq_scales_at_a_4_byte_offset(threads):
+@pytest.mark.parametrize("shape", SHAPES)
+def test_irq_scales_at_a_4_byte_offset(shape):
     # FP32 scales that are 4- but not 16-byte aligned take the per-block
     # stores; the default-aligned ones take the gathered 16-byte store
-    rq.set_block_threads(threads)
-    cfg = dict(synth.IRQ_TINY, N=23, H=16, hpg=8, max_pos=65536, seed=170)
+    N, G, hpg = table_tokens(shape, 16, base=23), 2, 8
+    cfg = dict(synth.IRQ_TINY, N=N, H=16, hpg=hpg, max_pos=65536, seed=170)
     o, pos, cache = synth.irq_inputs(cfg)
-    N, G, hpg = 23, 2, 8
-    print(f"[case] irq scales at +4 bytes threads={threads}", flush=True)
+    print(f"[case] irq scales at +4 bytes {shape}", flush=True)
     out = torch.full((G, N, hpg * 512), 0xCD, dtype=torch.uint8, device=DEV)
     raw = torch.full((G * N * hpg * 4 + 1,), -7.0, dtype=torch.float32, device=DEV)
     sc = raw[1:].view(G, N, hpg * 4)
