@@ -500,8 +500,9 @@ def cold_single_us(fn, scratch, reps=21):
 
 
 def bench_decode(args, device, stream):
-    """Decode sizes: per call through Python (host-bound), in a HIP graph
-    (GPU-side cost with warm caches), and one cold launch on its own."""
+    """Decode sizes: per call through Python (host-bound), through a prepared
+    call (checks and marshalling done once), in a HIP graph (GPU-side cost
+    with warm caches), and one cold launch on its own."""
     import torch
 
     import rope_fp8_quant_amd as rq
@@ -525,12 +526,18 @@ def bench_decode(args, device, stream):
 
         ms = time_launches(irq, 200, 20, stream)
         msq = time_launches(qnr, 200, 20, stream)
+        irq_p = rq.prepare(rq.inv_rope_fp8_quant, od, pd, cache, 8, out, sc)
+        qnr_p = rq.prepare(rq.qnorm_rope, q, None, pd, cache, q_out, 1e-6)
+        msp = time_launches(irq_p, 200, 20, stream)
+        msqp = time_launches(qnr_p, 200, 20, stream)
         gi, gq = graph_per_call_us(irq), graph_per_call_us(qnr)
         ci, cq = cold_single_us(irq, scratch), cold_single_us(qnr, scratch)
-        res[f"N{N}"] = dict(irq_us_python=round(ms * 1e3, 2), irq_us_graph=round(gi, 2),
+        res[f"N{N}"] = dict(irq_us_python=round(ms * 1e3, 2),
+                            irq_us_prepared=round(msp * 1e3, 2), irq_us_graph=round(gi, 2),
                             irq_gbs_graph=round(irq_bytes(N, 32) / gi / 1e3, 1),
                             irq_us_single_cold=round(ci, 2),
-                            qnr_us_python=round(msq * 1e3, 2), qnr_us_graph=round(gq, 2),
+                            qnr_us_python=round(msq * 1e3, 2),
+                            qnr_us_prepared=round(msqp * 1e3, 2), qnr_us_graph=round(gq, 2),
                             qnr_gbs_graph=round(qnr_bytes(N, 32, 128) / gq / 1e3, 1),
                             qnr_us_single_cold=round(cq, 2))
     del scratch

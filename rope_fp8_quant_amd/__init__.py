@@ -18,16 +18,18 @@ full-cache forms (section 2), and of vLLM PR
 #46862 ("vLLM의 GLM5.2 성능 최적화: Triton 커널 융합을 통한 E2E Throughput 향상",
 section 1) for ``indexer_q_rope_quant``.
 """
+import threading
+
 import torch
 
-from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, lib
+from ._lib import RQ_SCALE_FP32, RQ_SCALE_UE8M0, RopeQuantError, check, functions, lib
 
 __all__ = [
     "inv_rope_fp8_quant", "inv_rope_bf16", "qnorm_rope", "qnorm_rope_fp8",
     "kv_rope_quant_insert", "kv_rope_insert_full", "qnorm_rope_kv_rope_quant_insert",
     "qnorm_rope_kv_rope_insert_full", "qnorm_rope_fp8_kv_rope_insert_full",
     "indexer_q_rope_quant", "empty_inv_rope_fp8_quant_outputs", "empty_qnorm_rope_fp8_outputs",
-    "empty_kv_cache", "abi_version", "RopeQuantError", "RECORD_BYTES",
+    "empty_kv_cache", "abi_version", "prepare", "Prepared", "RopeQuantError", "RECORD_BYTES",
     "SCALE_FMTS",
 ]
 
@@ -57,32 +59,74 @@ def _same_device(ref, *named):
             raise ValueError(f"{name} must be on {ref.device}")
 
 
-# torch's handle of the current stream of a device, without building a Stream
-# object (falls back to the public API where this build lacks it)
+# torch's handle of the current stream of a device and its current device
+# index, without building Stream / device objects (the public API where this
+# build lacks them)
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+
+# A prepare() call in progress on this thread collects the launch here
+# instead of launching it.
+_capture = threading.local()
 
 
-def _call(name, device, stream, *args):
-    """Launch C entry point `name` on `stream` (default: torch's current stream
-    of `device`), with `device` current during the call, and raise on a
-    non-OK status.  The library launches on the current HIP device, so a
-    stream or tensors on another device would hand it foreign pointers."""
-    idx = device.index
+def _launch(name, fn, idx, stream, args):
     if stream is None:
         handle = (_raw_stream(idx) if _raw_stream is not None
-                  else torch.cuda.current_stream(device).cuda_stream)
+                  else torch.cuda.current_stream(idx).cuda_stream)
     else:
-        if stream.device != device:
-            raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+        if stream.device.index != idx:
+            raise ValueError(f"stream is on {stream.device}, the tensors on cuda:{idx}")
         handle = stream.cuda_stream
-    fn = getattr(lib(), name)
-    if idx != torch.cuda.current_device():
+    if idx != _get_device():
         with torch.cuda.device(idx):
             rc = fn(*args, handle)
     else:
         rc = fn(*args, handle)
     if rc:
         check(name, rc)
+
+
+def _call(name, idx, stream, *args):
+    """Launch C entry point `name` on `stream` (default: torch's current stream
+    of device `idx`), with that device current during the call, and raise on a
+    non-OK status.  The library launches on the current HIP device, so a
+    stream or tensors on another device would hand it foreign pointers."""
+    if getattr(_capture, "slot", None) is not None:
+        _capture.slot.append((name, idx, args))
+        return
+    _launch(name, functions()[name], idx, stream, args)
+
+
+class Prepared:
+    """One op call with its arguments checked and marshalled once: calling it
+    launches the same work again (on `stream`, default torch's current stream
+    of the tensors' device) with no further checks.  It keeps its tensors
+    alive; they must keep their storage (no resize or set_) and are read and
+    written again on every call."""
+
+    __slots__ = ("name", "_fn", "_idx", "_args", "_keep")
+
+    def __init__(self, name, idx, args, keep):
+        self.name, self._fn, self._idx, self._args, self._keep = (
+            name, functions()[name], idx, args, keep)
+
+    def __call__(self, stream=None):
+        _launch(self.name, self._fn, self._idx, stream, self._args)
+
+
+def prepare(op, *args, **kwargs):
+    """Check and marshal `op(*args, **kwargs)` once (any op of this module) and
+    return a Prepared call that relaunches it: for loops that run the same op
+    on the same buffers, where the per-call checks would cost more host time
+    than the kernel."""
+    _capture.slot = []
+    try:
+        op(*args, **kwargs)
+        (name, idx, cargs), = _capture.slot
+    finally:
+        _capture.slot = None
+    return Prepared(name, idx, cargs, (args, kwargs))
 
 
 def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
@@ -155,7 +199,7 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
         raise ValueError(f"fp32 scales must be float32 [{G}, {N}, {hpg * 4}]")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"),
                  (scales, "scales"))
-    _call("inv_rope_fp8_quant", o.device, stream,
+    _call("inv_rope_fp8_quant", o.get_device(), stream,
         o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], N, H, hpg, fmt, float(eps),
         out.data_ptr(), out.stride(0), out.stride(1),
@@ -185,7 +229,7 @@ def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None
             out.stride(2) != 1):
         raise ValueError(f"out must be bf16 [{G}, {N}, {hpg * 512}], last dim contiguous")
     _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"))
-    _call("inv_rope_bf16", o.device, stream,
+    _call("inv_rope_bf16", o.get_device(), stream,
         o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], N, H, hpg, out.data_ptr(), out.stride(0), out.stride(1))
 
@@ -276,7 +320,7 @@ def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, str
     norm_weight: bf16 [512] or None.  With q_head_padded == Hq, q_out may be
     q_in itself (contiguous): each head is read before it is written."""
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
-    _call("qnorm_rope", q_in.device, stream,
+    _call("qnorm_rope", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
         cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, q_out.shape[1], float(eps),
@@ -291,7 +335,7 @@ def qnorm_rope_fp8(q_in, norm_weight, positions, cos_sin_cache, q_fp8, q_scales,
     fmt = _fmt(scale_fmt)
     N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
-    _call("qnorm_rope_fp8", q_in.device, stream,
+    _call("qnorm_rope_fp8", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
         cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, hpad, float(eps), fmt,
@@ -303,7 +347,7 @@ def kv_rope_insert_full(kv, positions, cos_sin_cache, slot_mapping, cache, strea
     [num_slots, >= 512]: token t's row goes to cache[slot_mapping[t], :512]
     (skipped for a negative slot)."""
     N = _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache)
-    _call("kv_rope_insert_full", kv.device, stream,
+    _call("kv_rope_insert_full", kv.get_device(), stream,
         kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, cache.data_ptr(), cache.shape[0],
         cache.stride(0))
@@ -316,7 +360,7 @@ def kv_rope_quant_insert(kv, positions, cos_sin_cache, slot_mapping, k_cache, ca
     k_cache [num_blocks, block_bytes] (block stride = k_cache.stride(0))."""
     fmt = _fmt(scale_fmt)
     N = _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size)
-    _call("kv_rope_quant_insert", kv.device, stream,
+    _call("kv_rope_quant_insert", kv.get_device(), stream,
         kv.data_ptr(), kv.stride(0), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], slot_mapping.data_ptr(), N, k_cache.data_ptr(), k_cache.shape[0],
         k_cache.stride(0), int(cache_block_size), fmt, float(eps))
@@ -330,7 +374,7 @@ def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_ca
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
     if _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    _call("qnorm_rope_kv_rope_quant_insert", q_in.device, stream,
+    _call("qnorm_rope_kv_rope_quant_insert", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
@@ -346,7 +390,7 @@ def qnorm_rope_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cac
     N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    _call("qnorm_rope_kv_rope_insert_full", q_in.device, stream,
+    _call("qnorm_rope_kv_rope_insert_full", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
@@ -364,7 +408,7 @@ def qnorm_rope_fp8_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
-    _call("qnorm_rope_fp8_kv_rope_insert_full", q_in.device, stream,
+    _call("qnorm_rope_fp8_kv_rope_insert_full", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
         None if norm_weight is None else norm_weight.data_ptr(), kv.data_ptr(), kv.stride(0),
         positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
@@ -393,7 +437,7 @@ def indexer_q_rope_quant(q, positions, cos_sin_cache, weights, q_fp8, weights_ou
         raise ValueError("q_fp8 must be uint8/float8_e4m3fn [N, H, 128], last dim contiguous")
     _same_device(q, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
                  (weights, "weights"), (q_fp8, "q_fp8"), (weights_out, "weights_out"))
-    _call("indexer_q_rope_quant", q.device, stream,
+    _call("indexer_q_rope_quant", q.get_device(), stream,
         q.data_ptr(), q.stride(0), q.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
         cos_sin_cache.shape[0], weights.data_ptr(), weights.stride(0), N, H,
         float(softmax_scale), float(head_scale), float(eps), q_fp8.data_ptr(), q_fp8.stride(0),

@@ -82,6 +82,18 @@ def lib():
     return _lib
 
 
+_fns = None
+
+
+def functions():
+    """The exported C entry points by name (looked up once)."""
+    global _fns
+    if _fns is None:
+        L = lib()
+        _fns = {n: getattr(L, n) for n in EXPORTS}
+    return _fns
+
+
 def check(fn, status):
     if status != RQ_OK:
         raise RopeQuantError(fn, status, lib().ropequant_strerror(status).decode())

@@ -931,25 +931,19 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
 
 // ---------------------------------------------------- indexer query path
 
-// One 128-dim indexer head per 16-lane row.  Lane L holds dims [4L, 4L+4)
-// (the rotated half, dims 0..63) and [64+4L, 64+4L+4) (passed through), read
-// as two 8-byte loads, so every load instruction covers whole 128-byte halves
-// of 4 heads.  Rotate-half pairs (i, i+32) then sit in lanes L and L^8: one
-// DPP row rotation by 8 brings each lane its partner's 4 values, and all 16
-// lanes rotate 4 values each (a layout with 8 consecutive dims per lane left
-// half the lanes idle through the rotation and took 31% more VALU
-// instructions; this one measured 5.7% faster).
-//
-// Work is dealt in items of 4 consecutive heads of one token (a token's last
-// item may hold fewer).  The item's token, position, cos/sin row and base
-// addresses are then wave-uniform and live in scalar registers; each lane
-// only adds an offset fixed for the whole kernel.  (Per-lane 64-bit address
-// arithmetic had made the kernel issue-bound: 291 VALU instructions per
-// wave, 26 of them quarter-rate 64-bit multiplies; now 188.)  A wave takes
-// kIdxRounds items, its loads issued before the first item's arithmetic.
-// The weight is read where lane 0 folds it; the compiler sinks the first
-// item's weight load into that branch, which timed 4% faster than forcing
-// it up front and 12% faster than sinking both.
+// A wave takes four work items, each 4 consecutive heads of one token (a
+// token's last item may hold fewer): 16 heads of 128 dims.  The item's token,
+// position, cos/sin row and base addresses are wave-uniform and live in
+// scalar registers.  Each load instruction reads one item's four 256-byte
+// head rows, 16 bytes per lane (1 KiB, contiguous when the heads are), and an
+// LDS transpose hands lane (row i, L) the 8-dim chunks 8s + {0, 32, 64, 96}
+// of head L >> 2 of item i (s = L & 3).  Every rotate-half pair (j, j + 32)
+// then sits in one lane, every lane rotates 8 pairs, and a head's amax is a
+// quad max.  The codes go back through LDS so that each store instruction
+// writes two items' 512-byte code rows, 16 bytes per lane.  (An earlier
+// layout, one head per 16-lane row with 8-byte loads and two items per wave,
+// kept 2 KiB in flight per wave and streamed at 6.0 TB/s for large launches;
+// this one streams at 7.1 TB/s.)
 struct IdxParams {
   LaunchHdr hdr;
   const uint16_t* q;
@@ -967,120 +961,155 @@ struct IdxParams {
   int64_t out_st, out_sh;
   float* wo;
   int64_t wo_st;
+  uint32_t out16;  // code rows 16-byte aligned (base and both strides)
 };
 
-constexpr int kIdxRounds = 2;    // items per wave (2 timed best of 1 to 4)
-
-constexpr int kRowRor8 = 0x128;  // lane i <- lane i^8 within the row (rotate by 8 of 16)
-
-__device__ __forceinline__ uint2 load_nt8(const uint8_t* p) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t v = __builtin_nontemporal_load((__attribute__((address_space(1))) const u32x2_t*)p);
-  return make_uint2(v.x, v.y);
-}
-
-template <int ROUNDS>
-__device__ __forceinline__ void idx_items(const IdxParams& p, uint32_t item0, int lane) {
-  const int q = lane >> 4, L = lane & 15;
-  // Row q of an item is head 4g + q; the host keeps these offsets in 32 bits.
-  const uint32_t q_row_off = (uint32_t)q * (uint32_t)p.q_sh * 2u;
-  const uint32_t o_row_off = (uint32_t)q * (uint32_t)p.out_sh;
-  uint32_t tj[ROUNDS], h0j[ROUNDS], nvj[ROUNDS];
-  uint2 ra[ROUNDS], rb[ROUNDS];
-  // Item j's head rows.  A slot past the last item repeats the last item, and
-  // a row past the token's last head reads the item's first row: every read
-  // stays inside q, and neither stores anything.
+// LDS slots (16 bytes) of item i: head row hh, 16-byte granule g at
+// 64 i + 16 hh + (g ^ 4 (hh & 1)), so the lanes of a read group hit distinct
+// banks.  Codes: head hh's 8-byte piece at byte 32 c + 8 s of its 128-byte
+// row is kept at 512 i + 128 hh + ((32 c + 8 s) ^ 32 (hh & 3)).
+__global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = lane >> 4, L = lane & 15, hh = L >> 2, sub = L & 3;
+  uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
+  const uint32_t item0 = wave_index(p.hdr) * 4u;
+  // The wave's four items, wave-uniform.  A slot past the last item repeats
+  // the last item, and a head past the token's last reads the item's first
+  // head: every read stays inside q, and neither stores anything.
+  uint32_t tk[4], h0k[4], nvk[4];
+  const uint8_t* qk[4];
+  int64_t posk[4];
 #pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) {
-    const uint32_t i = min(item0 + j, p.items - 1u);
-    const uint32_t t = magic_div(i, p.div_quads);
-    const uint32_t h0 = 4u * (i - t * p.quads);
-    tj[j] = t;
-    h0j[j] = h0;
-    nvj[j] = min(4u, p.n_heads - h0);
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(p.q + (int64_t)t * p.q_st +
-                                                           (int64_t)h0 * p.q_sh);
-    const uint32_t off = ((uint32_t)q < nvj[j] ? q_row_off : 0u) + 8u * L;
-    ra[j] = load_nt8(base + off);
-    rb[j] = load_nt8(base + off + 128);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t it = min(item0 + k, p.items - 1u);
+    const uint32_t t = magic_div(it, p.div_quads);
+    tk[k] = t;
+    h0k[k] = 4u * (it - t * p.quads);
+    nvk[k] = (item0 + k < p.items) ? min(4u, p.n_heads - h0k[k]) : 0u;
+    qk[k] = reinterpret_cast<const uint8_t*>(p.q + (int64_t)t * p.q_st + (int64_t)h0k[k] * p.q_sh);
+    posk[k] = load_uniform(p.positions + t);
   }
-  int64_t pos[ROUNDS];
+  // Reads: instruction k, lane L' -> head L' >> 4 of item k, granule L' & 15.
+  const uint32_t lhead = (uint32_t)lane >> 4;
+  uint4 raw[4];
 #pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) pos[j] = load_uniform(p.positions + tj[j]);
-  float4 cv[ROUNDS], sv[ROUNDS];
-  float wg[ROUNDS];
-  bool bad[ROUNDS];
-#pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) {
-    bad[j] = pos[j] < 0 || pos[j] >= p.max_pos;
-    const float4* row = reinterpret_cast<const float4*>(p.cs + (bad[j] ? 0 : pos[j]) * 64);
-    cv[j] = row[L & 7];
-    sv[j] = row[8 + (L & 7)];
-    const float* wrow = p.w + (int64_t)tj[j] * p.w_st + h0j[j];
-    wg[j] = wrow[(uint32_t)q < nvj[j] ? q : 0];
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t nv = max(nvk[k], 1u);
+    const uint32_t off = (lhead < nv ? lhead * (uint32_t)p.q_sh * 2u : 0u) + 16u * (lane & 15);
+    raw[k] = load_nt(qk[k] + off);
   }
-  // Lanes 0..7 hold dims i < 32 and subtract their partner's term: flipping
-  // the partner's sign bits is exact and gives the same products.
-  const uint32_t flip = L < 8 ? 0x80008000u : 0u;
+  const float* csk[4];
+  uint32_t badk[4];
 #pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) {
-    const uint32_t pw[2] = {dpp_u32<kRowRor8>(ra[j].x) ^ flip, dpp_u32<kRowRor8>(ra[j].y) ^ flip};
-    const uint32_t ow[2] = {ra[j].x, ra[j].y};
-    const float c4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
-    const float s4[4] = {sv[j].x, sv[j].y, sv[j].z, sv[j].w};
-    float x[8];
+  for (int k = 0; k < 4; ++k) {
+    const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
+    badk[k] = bad;
+    csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+  }
+  // cos / sin of the lane's 8 pairs: columns 8s .. 8s + 7 of its item's row
+  const float4* csrow = reinterpret_cast<const float4*>(PICK_ROW(row, csk));
+  const float4 c0 = csrow[2 * sub], c1 = csrow[2 * sub + 1];
+  const float4 s0 = csrow[8 + 2 * sub], s1 = csrow[8 + 2 * sub + 1];
+  // transpose through LDS
+  const int wslot = lane ^ (((lane >> 4) & 1) << 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  for (int k = 0; k < 4; ++k) lds_wave[64 * k + wslot] = raw[k];
+  wave_lds_sync();
+  uint4 w[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = 2 * i + h;
-        const float own = h ? bf_hi(ow[i]) : bf_lo(ow[i]);
-        const float prt = h ? bf_hi(pw[i]) : bf_lo(pw[i]);
-        const float y = own * c4[e] + prt * s4[e];
-        x[e] = (float)(__bf16)y;
-      }
+  for (int c = 0; c < 4; ++c) w[c] = lds_wave[64 * row + 16 * hh + 4 * (c ^ (hh & 1)) + sub];
+
+  // rotate-half on chunks 0 (dims 8s + j) and 1 (dims 32 + 8s + j), each
+  // result rounded to bf16 and back; chunks 2, 3 pass through
+  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  float x[4][8];
+  {
+    const uint32_t e4[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+    const uint32_t o4[4] = {w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = (j & 1) ? bf_hi(e4[j >> 1]) : bf_lo(e4[j >> 1]);
+      const float o = (j & 1) ? bf_hi(o4[j >> 1]) : bf_lo(o4[j >> 1]);
+      const float a = e * cv[j], b = o * sv[j], d = o * cv[j], f = e * sv[j];
+      x[0][j] = (float)(__bf16)(a - b);
+      x[1][j] = (float)(__bf16)(d + f);
     }
-    x[4] = bf_lo(rb[j].x);
-    x[5] = bf_hi(rb[j].x);
-    x[6] = bf_lo(rb[j].y);
-    x[7] = bf_hi(rb[j].y);
-    float m = 0.0f;
+    const uint32_t p2[4] = {w[2].x, w[2].y, w[2].z, w[2].w};
+    const uint32_t p3[4] = {w[3].x, w[3].y, w[3].z, w[3].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
-    m = max_dpp_nonneg<kQuadSwap1>(m);
-    m = max_dpp_nonneg<kQuadSwap2>(m);
-    m = max_dpp_nonneg<kRowHalfMirror>(m);
-    m = max_dpp_nonneg<kRowMirror>(m);
-    m = __builtin_fmaxf(m, p.eps);
-    const uint32_t tb = __builtin_bit_cast(uint32_t, m < __builtin_inff() ? div448(m) : m);
-    const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
-    const float qs = pow2_f32(kexp);
-    const float mult = pow2_neg_f32(kexp);
-    uint32_t code[2];
+    for (int j = 0; j < 4; ++j) {
+      x[2][2 * j] = bf_lo(p2[j]);
+      x[2][2 * j + 1] = bf_hi(p2[j]);
+      x[3][2 * j] = bf_lo(p3[j]);
+      x[3][2 * j + 1] = bf_hi(p3[j]);
+    }
+  }
+  float m = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float a0 = x[4 * h] * mult, a1 = x[4 * h + 1] * mult;
-      const float a2 = x[4 * h + 2] * mult, a3 = x[4 * h + 3] * mult;
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(x[c][j]));
+  m = max_dpp_nonneg<kQuadSwap1>(m);
+  m = max_dpp_nonneg<kQuadSwap2>(m);
+  m = __builtin_fmaxf(m, p.eps);
+  const uint32_t tb = __builtin_bit_cast(uint32_t, m < __builtin_inff() ? div448(m) : m);
+  const int kexp = (int)((tb >> 23) & 0xFFu) - 127 + ((tb & 0x7FFFFFu) ? 1 : 0);
+  const float qs = pow2_f32(kexp);
+  const float mult = pow2_neg_f32(kexp);
+  uint32_t code[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const float a0 = x[c][4 * hf] * mult, a1 = x[c][4 * hf + 1] * mult;
+      const float a2 = x[c][4 * hf + 2] * mult, a3 = x[c][4 * hf + 3] * mult;
       int wd = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __builtin_bit_cast(int, a0), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, wd, true);
-      code[h] = (uint32_t)wd;
+      code[2 * c + hf] = (uint32_t)wd;
     }
-    if (item0 + j < p.items && (uint32_t)q < nvj[j]) {
-      uint8_t* orow = p.out + (int64_t)tj[j] * p.out_st + (int64_t)h0j[j] * p.out_sh;
-      const uint32_t off = o_row_off + 4u * L;
-      __builtin_nontemporal_store(code[0], (__attribute__((address_space(1))) uint32_t*)(orow + off));
-      __builtin_nontemporal_store(code[1], (__attribute__((address_space(1))) uint32_t*)(orow + off + 64));
-      if (L == 0) {
-        const float fold = ((wg[j] * qs) * p.softmax_scale) * p.head_scale;
-        p.wo[(int64_t)tj[j] * p.wo_st + h0j[j] + q] = bad[j] ? __builtin_nanf("") : fold;
+  }
+  // folded weight of the lane's head (lane s == 0 of the quad)
+  const uint32_t nv = PICK_ROW(row, nvk);
+  if (sub == 0 && (uint32_t)hh < nv) {
+    const uint32_t t = PICK_ROW(row, tk), h = PICK_ROW(row, h0k) + (uint32_t)hh;
+    const float wv = p.w[(int64_t)t * p.w_st + h];
+    const float fold = ((wv * qs) * p.softmax_scale) * p.head_scale;
+    p.wo[(int64_t)t * p.wo_st + h] = PICK_ROW(row, badk) ? __builtin_nanf("") : fold;
+  }
+  // codes through LDS (the transpose reads are done before the slice is reused)
+  wave_lds_sync();
+  uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    lds8[64 * row + 16 * hh + ((4 * c + sub) ^ (4 * (hh & 3)))] =
+        make_uint2(code[2 * c], code[2 * c + 1]);
+  wave_lds_sync();
+  // store instruction j: lanes 0..31 item 2j, lanes 32..63 item 2j + 1; lane
+  // granule g = lane & 31 is head g >> 3, bytes 16 (g & 7) of its code row
+  const uint32_t g = (uint32_t)lane & 31u, sh = g >> 3, gg = g & 7u;
+  const int half = lane >> 5;
+  const uint4* lds16 = reinterpret_cast<const uint4*>(lds_wave);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int k0 = 2 * j, k1 = 2 * j + 1;  // the instruction's two items
+    const uint4 v = lds16[32 * (k0 + half) + 8 * sh + 2 * ((gg >> 1) ^ (sh & 3)) + (gg & 1)];
+    const uint32_t nvi = half ? nvk[k1] : nvk[k0];
+    uint8_t* const base = half ? p.out + (int64_t)tk[k1] * p.out_st + (int64_t)h0k[k1] * p.out_sh
+                               : p.out + (int64_t)tk[k0] * p.out_st + (int64_t)h0k[k0] * p.out_sh;
+    if (sh < nvi) {
+      uint8_t* const dst = base + (int64_t)sh * p.out_sh + 16 * gg;
+      if (p.out16) {
+        store_nt(dst, v);
+      } else {  // 8-byte aligned rows
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(1))) u32x2_t* gptr2;
+        __builtin_nontemporal_store(u32x2_t{v.x, v.y}, (gptr2)dst);
+        __builtin_nontemporal_store(u32x2_t{v.z, v.w}, (gptr2)(dst + 8));
       }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
-  const int lane = threadIdx.x & 63;
-  idx_items<kIdxRounds>(p, wave_index(p.hdr) * kIdxRounds, lane);
 }
 
 // ------------------------------------------------------------ host side
@@ -1629,9 +1658,10 @@ int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_st
   p.softmax_scale = (float)softmax_scale; p.head_scale = (float)head_scale; p.eps = (float)eps;
   p.out = q_fp8; p.out_st = out_stride_token; p.out_sh = out_stride_head;
   p.wo = weights_out; p.wo_st = wo_stride_token;
-  // kIdxRounds items per wave; `launch` sizes grids in 16-lane rows, 4 per wave
-  const uint32_t rows = 4u * ((p.items + kIdxRounds - 1) / kIdxRounds);
-  return launch((const void*)idx_kernel, rows, kIdxShape, &p, (hipStream_t)stream, false);
+  p.out16 = aligned(q_fp8, 16) && out_stride_token % 16 == 0 && out_stride_head % 16 == 0;
+  // one item per 16-lane row, four per wave
+  const uint32_t rows = 4u * ((p.items + 3u) / 4u);
+  return launch((const void*)idx_kernel, rows, kIdxShape, &p, (hipStream_t)stream);
 }
 
 }  // extern "C"
