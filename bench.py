@@ -178,8 +178,9 @@ def bench_stream(args, device, stream):
     """What HBM sustains on this part for the kernels' access patterns, with
     no arithmetic: 512 MiB of 1 KiB rows read (nontemporal), written
     (nontemporal, plain, sc1), and inv_rope_fp8_quant's traffic for the
-    prefill workload's 524288 units; each over rotating buffers like the
-    kernels.  Also the fixed cost of one empty launch, eager and in a graph."""
+    prefill workload's 524288 units and for the unit counts of the shorter
+    launches; each over rotating buffers like the kernels.  Also the fixed
+    cost of one empty launch, eager and in a graph."""
     import torch
     L = stream_lib()
 
@@ -220,6 +221,22 @@ def bench_stream(args, device, stream):
                                     ms * 1e3, b), buffer_sets=sets)
     del rot, fns
     torch.cuda.empty_cache()
+    # the same pattern at the sizes of the shorter launches: a launch's fixed
+    # cost weighs more on fewer bytes, for a plain stream as for a kernel
+    for key, units, what in SAME_SIZE_STREAMS:
+        b = units * (1024 + 512 + 16)
+        sets = rotation_sets(b)
+        rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
+                torch.empty(units * 512, dtype=torch.uint8, device=device),
+                torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
+        fns = [lambda s_=s_, c=c, sc=sc, u=units: _ok(
+            L.bench_stream_irq(s_.data_ptr(), c.data_ptr(), sc.data_ptr(), u, h()), "irq")
+            for s_, c, sc in rot]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
+        res[key] = dict(_rate(f"the same pattern for {units} units ({what}), no math",
+                              ms * 1e3, b), buffer_sets=sets)
+        del rot, fns
+        torch.cuda.empty_cache()
 
     def empty():
         _ok(L.bench_stream_empty(h()), "empty")
@@ -271,6 +288,27 @@ def bench_irq(args, device, stream, fmt="fp32", same_buffers=False):
     return cfg, ms, (o, pos, cache), sets
 
 
+# Streaming-pattern sizes matched to shorter launches: (ceiling key, 512-dim
+# units of 1 KiB read and 528 B written, the kernel it stands beside).  The
+# indexer moves 1 KiB in and 544 B out per 4-head item, 65536 items at 4096
+# tokens x 64 heads; the irregular IRQ 4096 x 48 units.
+SAME_SIZE_STREAMS = (
+    ("irq_pattern_196608_units", 4096 * 48, "inv_rope_fp8_quant_irregular"),
+    ("irq_pattern_65536_units", 4096 * 16, "indexer_q_rope_quant"),
+)
+
+
+def vs_same_size_stream(extra, ceiling):
+    """Beside each shorter launch, the streaming pattern's rate at its size."""
+    if not ceiling:
+        return
+    for key, _, what in SAME_SIZE_STREAMS:
+        if what in extra and key in ceiling:
+            extra[what]["same_size_stream_gbs"] = round(ceiling[key]["gbs"], 1)
+            extra[what]["frac_of_same_size_stream"] = round(
+                extra[what]["gbs"] / ceiling[key]["gbs"], 4)
+
+
 # Filled by bench_stream when it runs: the empty-launch cost in a graph and
 # the streaming rate of inv_rope_fp8_quant's byte pattern, for the estimate
 # beside short launches.
@@ -315,7 +353,17 @@ def bench_qnr_kvi(args, device, stream):
         del qd, rot, fns
     if args.only in (None, "kvi"):
         cfg = synth.KVI_FORWARD
+        if args.kvi_tokens is not None or args.kvi_slots == "seq":
+            # a traffic probe of the same op: another token count (the cache
+            # grows to twice the tokens when 16384 slots are too few) or
+            # slots in token order
+            n = cfg["N"] if args.kvi_tokens is None else args.kvi_tokens
+            cfg = dict(cfg, N=n, num_blocks=max(cfg["num_blocks"], -(-2 * n // cfg["block_size"])),
+                       max_pos=max(cfg["max_pos"], n))
+            cfg["name"] = f"kvi_n{n}_{cfg['num_blocks']}x{cfg['block_size']}_{args.kvi_slots}"
         kv, pos, slots, cache = synth.kvi_inputs(cfg)
+        if args.kvi_slots == "seq":
+            slots = np.arange(cfg["N"], dtype=np.int64)
         kd, pd, sd, cd = (to_dev(x, device) for x in (kv, pos, slots, cache))
         k_cache = rq.empty_kv_cache(cfg["num_blocks"], cfg["block_size"], device, fill=0xAA)
         b = kvi_bytes(cfg["N"])
@@ -327,6 +375,8 @@ def bench_qnr_kvi(args, device, stream):
         res["kv_rope_quant_insert"] = small_launch_record(
             cfg["name"], b, graph_rotating_per_call_us(fns), ms * 1e3, sets)
         del rot, fns
+        if cfg is not synth.KVI_FORWARD:
+            return res
         # the same q and kv work in one launch (positions 0..8191 serve both)
         qc = synth.QNR_FORWARD
         q, w, qpos, qcache = synth.qnr_inputs(qc)
@@ -697,6 +747,112 @@ def traffic_from_profile():
     return rec.get("traffic_bytes_per_launch")
 
 
+# ---------------------------------------------------- rocprofv3 summaries
+
+def _csv_rows(path):
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
+    for f in files:
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _short(name):
+    """Kernel name without the parameter list and anonymous namespaces."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth, out = 0, []
+    for ch in name:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out)
+
+
+def counter_medians(path):
+    """{(kernel, grid, counter): (median value, dispatches)} from a rocprofv3
+    --pmc output directory (or its counter_collection CSV)."""
+    import statistics
+    vals = {}
+    for r in _csv_rows(path):
+        if "Counter_Name" not in r:
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])
+        vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (statistics.median(v), len(v)) for k, v in vals.items()}
+
+
+def trace_stats(path):
+    """{(kernel, grid, workgroup): [durations in us]} from a rocprofv3
+    --kernel-trace output directory (its kernel_trace CSV)."""
+    out = {}
+    for r in _csv_rows(path):
+        if "Start_Timestamp" not in r or "Counter_Name" in r or "Kernel_Name" not in r:
+            continue
+        grid = int(r.get("Grid_Size") or r["Grid_Size_X"])
+        wg = int(r.get("Workgroup_Size") or r["Workgroup_Size_X"])
+        key = (_short(r["Kernel_Name"]), grid, wg)
+        out.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
+def summarize(paths):
+    """Print per-kernel medians of every counter / trace directory given."""
+    import statistics
+    for path in paths:
+        print(f"## {path}")
+        med = counter_medians(path)
+        for (k, g, c), (v, n) in sorted(med.items()):
+            print(f"| {k} | {g:,} | {c} | {v:,.3f} | {n} |")
+        for (k, g, w), d in sorted(trace_stats(path).items(), key=lambda x: -sum(x[1])):
+            print(f"| {k} | {g:,} | {w} | {len(d)} | {sum(d) / len(d):.2f} | "
+                  f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+
+
+def write_counters_json(irq_fetch, irq_write, copy_fetch, copy_write, sq=None):
+    """profiles/irq_prefill_n16384_h32_counters.json from four rocprofv3 --pmc
+    runs: FETCH_SIZE and WRITE_SIZE of `bench.py --only irq` and of
+    `bench.py --only copy` (the calibration), plus optionally SQ counters."""
+    from rope_fp8_quant_amd import synth
+    cfg = synth.IRQ_PREFILL
+    N, H = cfg["N"], cfg["H"]
+    grid = N * H * 16  # 16 threads per unit
+
+    def pick(path, kernel, counter, grid_size=None):
+        for (k, g, c), (v, _) in counter_medians(path).items():
+            if k.startswith(kernel) and c == counter and (grid_size is None or g == grid_size):
+                return v
+        raise RuntimeError(f"{path}: no {counter} for {kernel}")
+    copy_bytes = 1 << 30
+    cf = pick(copy_fetch, "__amd_rocclr_copyBuffer", "FETCH_SIZE") * 1024 / copy_bytes
+    cw = pick(copy_write, "__amd_rocclr_copyBuffer", "WRITE_SIZE") * 1024 / copy_bytes
+    f = pick(irq_fetch, "irq_kernel<0>", "FETCH_SIZE", grid)
+    w = pick(irq_write, "irq_kernel<0>", "WRITE_SIZE", grid)
+    rd, wr = round(f * 1024 / cf), round(w * 1024 / cw)
+    alg_r = N * H * 1024 + N * (8 + 256)
+    alg_w = N * H * (512 + 16)
+    rec = {"kernel": "irq_kernel<0> (inv_rope_fp8_quant, fp32 scales)",
+           "workload": cfg["name"], "kernel_sha256_16": kernel_hash(),
+           "fetch_size_kib_per_dispatch": f, "write_size_kib_per_dispatch": w,
+           "calibration": {"kernel": "__amd_rocclr_copyBuffer, 1 GiB device copy "
+                                     "(bench.py --only copy)",
+                           "fetch_factor": cf, "write_factor": cw},
+           "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+           "traffic_bytes_per_launch": rd + wr,
+           "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+           "traffic_over_algorithmic": (rd + wr) / (alg_r + alg_w)}
+    if sq:
+        rec["sq_counters_per_dispatch"] = {
+            c: v for (k, g, c), (v, _) in counter_medians(sq).items()
+            if k.startswith("irq_kernel<0>") and g == grid}
+    with open(PROFILE_COUNTERS, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -707,11 +863,32 @@ def main():
     ap.add_argument("--only", choices=["irq", "qnr", "kvi", "idx", "variants", "decode", "copy",
                                        "stream"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kvi-tokens", type=int, default=None,
+                    help="with --only kvi: tokens inserted (default 8192)")
+    ap.add_argument("--kvi-slots", choices=["perm", "seq"], default="perm",
+                    help="with --only kvi: a seeded permutation of the slots (default) or "
+                         "slots 0..N-1 in token order")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print per-kernel medians of rocprofv3 output directories and exit")
+    ap.add_argument("--write-counters-json", nargs="+", metavar="DIR",
+                    help="IRQ_FETCH IRQ_WRITE COPY_FETCH COPY_WRITE [SQ]: write the counter "
+                         "record bench lines read their traffic from, and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.write_counters_json:
+        write_counters_json(*args.write_counters_json)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the hot path has no cross-GPU step and this "
-              "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path has no cross-GPU step, and "
+              "each GPU would run the same kernels on its own shard (run with --gpus 1).",
+              file=sys.stderr)
         sys.exit(2)
+    if (args.kvi_tokens is not None or args.kvi_slots != "perm") and args.only != "kvi":
+        ap.error("--kvi-tokens and --kvi-slots go with --only kvi")
+    if args.kvi_tokens is not None and not 1 <= args.kvi_tokens <= 1 << 20:
+        ap.error("--kvi-tokens must be in [1, 2^20]")
 
     import torch
 
@@ -725,7 +902,7 @@ def main():
         print(json.dumps({"copy_calibration": bench_copy(args, device, stream)}))
         return
     ceiling = None
-    if args.only in (None, "stream", "kvi", "variants"):
+    if args.only in (None, "stream", "kvi", "idx", "variants"):
         progress("streaming ceiling")
         ceiling = bench_stream(args, device, stream)
         CEILING.update(floor_us=ceiling["empty_launch"]["us_graph"],
@@ -735,8 +912,9 @@ def main():
         print(json.dumps({"stream_ceiling": ceiling}))
         return
     if args.only in ("qnr", "kvi", "idx"):
-        print(json.dumps({"extra": bench_qnr_kvi(args, device, stream),
-                          "stream_ceiling": ceiling}))
+        extra = bench_qnr_kvi(args, device, stream)
+        vs_same_size_stream(extra, ceiling)
+        print(json.dumps({"extra": extra, "stream_ceiling": ceiling}))
         return
     if args.only == "decode":
         print(json.dumps({"decode": bench_decode(args, device, stream)}))
@@ -805,6 +983,7 @@ def main():
         line["cpu_baseline_sharded"] = cpu_baseline_sharded(host_inputs)
     if extra:
         line["extra"] = extra
+    vs_same_size_stream(extra, ceiling)
     if ceiling:
         line["stream_ceiling"] = ceiling
         line["frac_of_stream_ceiling"] = round(gbs / ceiling["irq_pattern"]["gbs"], 4)

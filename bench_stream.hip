@@ -1,16 +1,20 @@
-// Streaming-ceiling kernels for bench.py (measurement only; not part of
-// libropequant's ABI).  They move bytes in the access patterns the library's
-// kernels use, with no arithmetic, so that bench.py can report what this
-// part's HBM actually sustains for each pattern beside what the kernels
-// reach:
+// Streaming kernels for bench.py (measurement only; not part of libropequant's
+// ABI).  They move bytes in the access patterns the library's kernels use,
+// with no arithmetic, so that bench.py can report what this part's HBM
+// sustains for each pattern beside what the kernels reach:
 //   * stream_read     - one 1 KiB row per 16-byte-per-lane nontemporal load
-//                       instruction, four rows per wave (the kernels' reads);
-//   * stream_write    - the same rows written with nontemporal, plain or
-//                       sc1-policy (buffer) 16-byte stores;
+//                       instruction, four rows per wave (the kernels' reads;
+//                       the row index is clamped rather than branched on, so
+//                       the four loads issue back to back);
+//   * stream_write    - 1 KiB rows written with nontemporal, plain or
+//                       sc1-policy (buffer) 16-byte stores, sixteen rows per
+//                       wave (timed fastest of 4, 8 and 16);
 //   * stream_irq      - inv_rope_fp8_quant's traffic per 512-dim unit: a 1 KiB
 //                       row read, 512 bytes and one 16-byte scale group
-//                       written, with the same workgroup size (128 threads)
-//                       and XCD chunking (64 workgroups);
+//                       written, with the kernel's workgroup size (128
+//                       threads), XCD chunking (64 workgroups) and its round
+//                       trip through LDS between the reads and the writes
+//                       (without that round trip the same bytes took 5% longer);
 //   * stream_empty    - a launch that does nothing: the fixed cost of one
 //                       launch on a stream.
 // Every kernel covers exactly `rows` rows; the host sizes the grid so that no
@@ -41,9 +45,10 @@ __device__ __forceinline__ uint32_t wave_id(uint32_t chunk_log2) {
                                         (threadIdx.x >> 6));
 }
 
-// Reads rows [4w, 4w + 4) of 1 KiB; a value is written to sink only when the
-// XOR of everything read equals `never` (chosen by the host as a value the
-// data cannot produce), which keeps the loads live.
+// Reads rows [4w, 4w + 4) of 1 KiB (a row past the end reads the last row
+// again); a value is written to sink only when the XOR of everything read
+// equals `never` (chosen by the host as a value the data cannot produce),
+// which keeps the loads live.
 __global__ __launch_bounds__(256) void stream_read(const uint8_t* src, uint64_t rows,
                                                    uint32_t never, uint32_t* sink) {
   const uint32_t lane = threadIdx.x & 63;
@@ -51,21 +56,24 @@ __global__ __launch_bounds__(256) void stream_read(const uint8_t* src, uint64_t 
   u32x4_t acc = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (r0 + k < rows)
-      acc ^= __builtin_nontemporal_load((gptr_c)(src + (r0 + k) * 1024 + 16 * lane));
+    const uint64_t r = r0 + k < rows ? r0 + k : rows - 1;
+    acc ^= __builtin_nontemporal_load((gptr_c)(src + r * 1024 + 16 * lane));
   }
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == never) sink[lane] = x;
 }
 
-// POLICY: 0 nontemporal, 1 plain, 2 sc1 through a buffer store on the row.
+// Writes rows [16w, 16w + 16).  POLICY: 0 nontemporal, 1 plain, 2 sc1
+// through a buffer store on the row.
+constexpr int kWriteRows = 16;
+
 template <int POLICY>
 __global__ __launch_bounds__(256) void stream_write(uint8_t* dst, uint64_t rows, uint32_t v) {
   const uint32_t lane = threadIdx.x & 63;
-  const uint64_t r0 = (uint64_t)wave_id(4) * 4;
+  const uint64_t r0 = (uint64_t)wave_id(4) * kWriteRows;
   const u32x4_t w = {v, v ^ lane, v + lane, ~v};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kWriteRows; ++k) {
     if (r0 + k >= rows) continue;
     uint8_t* row = dst + (r0 + k) * 1024;
     if (POLICY == 0) {
@@ -85,6 +93,7 @@ __global__ __launch_bounds__(256) void stream_write(uint8_t* dst, uint64_t rows,
 // 0 and 2, lanes 32..63 units 1 and 3, 16 bytes each.
 __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* codes,
                                                   uint8_t* scales, uint64_t units) {
+  extern __shared__ u32x4_t lds[];
   const uint32_t lane = threadIdx.x & 63;
   const uint64_t u0 = (uint64_t)wave_id(6) * 4;
   u32x4_t in[4];
@@ -93,6 +102,16 @@ __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* c
     const uint64_t u = u0 + k < units ? u0 + k : units - 1;
     in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
   }
+  // through the wave's 4 KiB of LDS and back, lanes permuted, as the kernel's
+  // transpose does
+  u32x4_t* slice = lds + 256 * (threadIdx.x >> 6);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) slice[64 * k + lane] = in[k];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) in[k] = slice[64 * k + (lane ^ 5)];
   const uint32_t half = lane >> 5, j = lane & 31;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -129,7 +148,7 @@ int bench_stream_read(const void* src, uint64_t rows, uint32_t never, void* sink
 
 int bench_stream_write(void* dst, uint64_t rows, int policy, void* stream) {
   if (rows == 0 || rows > (1ull << 36) || policy < 0 || policy > 2) return -1;
-  const dim3 g(grid_for(rows, 16)), b(256);
+  const dim3 g(grid_for(rows, 4 * kWriteRows)), b(256);
   const hipStream_t s = (hipStream_t)stream;
   if (policy == 0) hipLaunchKernelGGL(stream_write<0>, g, b, 0, s, (uint8_t*)dst, rows, 0x5A5Au);
   if (policy == 1) hipLaunchKernelGGL(stream_write<1>, g, b, 0, s, (uint8_t*)dst, rows, 0x5A5Au);
@@ -139,7 +158,7 @@ int bench_stream_write(void* dst, uint64_t rows, int policy, void* stream) {
 
 int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units, void* stream) {
   if (units == 0 || units > (1ull << 36)) return -1;
-  hipLaunchKernelGGL(stream_irq, dim3(grid_for(units, 8)), dim3(128), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(stream_irq, dim3(grid_for(units, 8)), dim3(128), 2 * 4096, (hipStream_t)stream,
                      (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
