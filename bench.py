@@ -101,8 +101,35 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+_SETTLE = {}
+
+
+def settle_clocks(ms=25.0):
+    """Keep the GPU busy with unrelated device work (a 256 MiB fill, over and
+    over) for about `ms` milliseconds before a measurement's warm-up.  Input
+    preparation on the host leaves the GPU idle for seconds, and after idle
+    the first ~100 launches (about 12 ms of work) run at lower clocks, more
+    than a warm-up of a few steps covers.  None of this is in a timed region,
+    and the warm-up and timed steps are still exactly the ones asked for."""
+    import time
+
+    import torch
+    buf = _SETTLE.get("buf")
+    if buf is None:
+        buf = _SETTLE["buf"] = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            buf.fill_(i & 0xFF)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_launches(fn, steps, warmup, stream):
     import torch
+    settle_clocks()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -160,7 +187,7 @@ def stream_lib():
         P, U64, U32, I = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
         L.bench_stream_read.argtypes = [P, U64, U32, P, P]
         L.bench_stream_write.argtypes = [P, U64, I, P]
-        L.bench_stream_irq.argtypes = [P, P, P, U64, P]
+        L.bench_stream_irq.argtypes = [P, P, P, U64, I, P]
         L.bench_stream_empty.argtypes = [P]
         for f in (L.bench_stream_read, L.bench_stream_write, L.bench_stream_irq,
                   L.bench_stream_empty):
@@ -207,36 +234,49 @@ def bench_stream(args, device, stream):
                          buffer_sets=sets)
     del bufs
     torch.cuda.empty_cache()
-    units = 16384 * 32
-    b = units * (1024 + 512 + 16)
-    sets = rotation_sets(b)
-    rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
-            torch.empty(units * 512, dtype=torch.uint8, device=device),
-            torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
-    fns = [lambda s_=s_, c=c, sc=sc: _ok(L.bench_stream_irq(s_.data_ptr(), c.data_ptr(),
-                                                             sc.data_ptr(), units, h()), "irq")
-           for s_, c, sc in rot]
-    ms = time_rotating(fns, args.steps, args.warmup, stream)
-    res["irq_pattern"] = dict(_rate("inv_rope_fp8_quant's bytes for 16384 x 32 units, no math",
-                                    ms * 1e3, b), buffer_sets=sets)
-    del rot, fns
-    torch.cuda.empty_cache()
-    # the same pattern at the sizes of the shorter launches: a launch's fixed
-    # cost weighs more on fewer bytes, for a plain stream as for a kernel
-    for key, units, what in SAME_SIZE_STREAMS:
+    # the pattern at the prefill workload's 524288 units, four units per
+    # wave as the kernel (and two, finer waves), then at the unit counts of
+    # the shorter launches: a launch's fixed cost weighs more on fewer bytes,
+    # for a plain stream as for a kernel
+    sizes = [("irq_pattern", 16384 * 32, "inv_rope_fp8_quant's bytes for 16384 x 32 units")]
+    sizes += [(key, units, f"the same pattern for {units} units ({what})")
+              for key, units, what in SAME_SIZE_STREAMS]
+    for key, units, what in sizes:
         b = units * (1024 + 512 + 16)
         sets = rotation_sets(b)
         rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
                 torch.empty(units * 512, dtype=torch.uint8, device=device),
                 torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
-        fns = [lambda s_=s_, c=c, sc=sc, u=units: _ok(
-            L.bench_stream_irq(s_.data_ptr(), c.data_ptr(), sc.data_ptr(), u, h()), "irq")
-            for s_, c, sc in rot]
-        ms = time_rotating(fns, args.steps, args.warmup, stream)
-        res[key] = dict(_rate(f"the same pattern for {units} units ({what}), no math",
-                              ms * 1e3, b), buffer_sets=sets)
-        del rot, fns
+        for upw, suffix in ((4, ""), (2, "_2_per_wave")):
+            fns = [lambda s_=s_, c=c, sc=sc, u=units, upw=upw: _ok(L.bench_stream_irq(
+                s_.data_ptr(), c.data_ptr(), sc.data_ptr(), u, upw, h()), "irq")
+                for s_, c, sc in rot]
+            ms = time_rotating(fns, args.steps, args.warmup, stream)
+            res[key + suffix] = dict(_rate(f"{what}, {upw} units per wave, no math", ms * 1e3, b),
+                                     buffer_sets=sets)
+            del fns
+        del rot
         torch.cuda.empty_cache()
+
+    # at the kv insert's size (8192 units, 12.7 MB), timed as that kernel is:
+    # per call inside a HIP graph, over enough buffer sets to total 1 GiB
+    units = 8192
+    b = units * (1024 + 512 + 16)
+    sets = rotation_sets(b)
+    rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
+            torch.empty(units * 512, dtype=torch.uint8, device=device),
+            torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
+    for upw, suffix in ((4, ""), (2, "_2_per_wave")):
+        fns = [lambda s_=s_, c=c, sc=sc, upw=upw: _ok(L.bench_stream_irq(
+            s_.data_ptr(), c.data_ptr(), sc.data_ptr(), units, upw, h()), "irq")
+            for s_, c, sc in rot]
+        us = graph_rotating_per_call_us(fns)
+        res["irq_pattern_8192_units" + suffix] = dict(
+            _rate(f"the same pattern for 8192 units (kv_rope_quant_insert's size), {upw} units "
+                  "per wave, no math, per call in a HIP graph", us, b), buffer_sets=sets)
+        del fns
+    del rot
+    torch.cuda.empty_cache()
 
     def empty():
         _ok(L.bench_stream_empty(h()), "empty")
@@ -299,7 +339,8 @@ SAME_SIZE_STREAMS = (
 
 
 def vs_same_size_stream(extra, ceiling):
-    """Beside each shorter launch, the streaming pattern's rate at its size."""
+    """Beside each shorter launch, the streaming pattern's rate at its size
+    (four units per wave, as the kernels, and two)."""
     if not ceiling:
         return
     for key, _, what in SAME_SIZE_STREAMS:
@@ -307,11 +348,16 @@ def vs_same_size_stream(extra, ceiling):
             extra[what]["same_size_stream_gbs"] = round(ceiling[key]["gbs"], 1)
             extra[what]["frac_of_same_size_stream"] = round(
                 extra[what]["gbs"] / ceiling[key]["gbs"], 4)
+            k2 = key + "_2_per_wave"
+            extra[what]["same_size_stream_2_per_wave_gbs"] = round(ceiling[k2]["gbs"], 1)
+            extra[what]["frac_of_same_size_stream_2_per_wave"] = round(
+                extra[what]["gbs"] / ceiling[k2]["gbs"], 4)
 
 
-# Filled by bench_stream when it runs: the empty-launch cost in a graph and
-# the streaming rate of inv_rope_fp8_quant's byte pattern, for the estimate
-# beside short launches.
+# Filled by bench_stream when it runs: the empty-launch cost in a graph, the
+# streaming rate of inv_rope_fp8_quant's byte pattern, and that pattern's
+# per-call time at the kv insert's size, for the comparisons beside short
+# launches.
 CEILING = {}
 
 
@@ -319,13 +365,16 @@ def small_launch_record(name, b, us_graph, us_python, sets):
     """A launch too short to time through Python: `us` is its per-call time in
     a HIP graph over rotating buffers; beside it the Python-loop time and,
     when the streaming ceiling was measured, the estimate of an empty launch
-    plus its bytes at the ceiling rate."""
+    plus its bytes at the ceiling rate, and the per-call time of the plain
+    streaming pattern at the kv insert's size, timed the same way."""
     rec = dict(_rate(name, us_graph, b), us_python=round(us_python, 3), buffer_sets=sets,
                timing="per call inside a HIP graph, call i on buffer set i mod buffer_sets")
     if CEILING:
         est = CEILING["floor_us"] + b / CEILING["gbs"] / 1e3
         rec.update(launch_floor_us=CEILING["floor_us"], ceiling_gbs=CEILING["gbs"],
-                   estimate_us=round(est, 3), residual_us=round(us_graph - est, 3))
+                   estimate_us=round(est, 3), residual_us=round(us_graph - est, 3),
+                   small_stream_us=CEILING["small_us"],
+                   small_stream_2_per_wave_us=CEILING["small_us_2"])
     return rec
 
 
@@ -518,6 +567,7 @@ def graph_per_call_us(fn, calls=100, replays=5):
         for _ in range(calls):
             fn()
     torch.cuda.synchronize()
+    settle_clocks()
     times = []
     for _ in range(replays + 1):
         a = torch.cuda.Event(enable_timing=True)
@@ -906,7 +956,9 @@ def main():
         progress("streaming ceiling")
         ceiling = bench_stream(args, device, stream)
         CEILING.update(floor_us=ceiling["empty_launch"]["us_graph"],
-                       gbs=round(ceiling["irq_pattern"]["gbs"], 1))
+                       gbs=round(ceiling["irq_pattern"]["gbs"], 1),
+                       small_us=round(ceiling["irq_pattern_8192_units"]["us"], 3),
+                       small_us_2=round(ceiling["irq_pattern_8192_units_2_per_wave"]["us"], 3))
         torch.cuda.empty_cache()
     if args.only == "stream":
         print(json.dumps({"stream_ceiling": ceiling}))
@@ -987,6 +1039,8 @@ def main():
     if ceiling:
         line["stream_ceiling"] = ceiling
         line["frac_of_stream_ceiling"] = round(gbs / ceiling["irq_pattern"]["gbs"], 4)
+        line["frac_of_stream_ceiling_2_per_wave"] = round(
+            gbs / ceiling["irq_pattern_2_per_wave"]["gbs"], 4)
     print(json.dumps(line), flush=True)
 
 

@@ -15,6 +15,8 @@
 //                       threads), XCD chunking (64 workgroups) and its round
 //                       trip through LDS between the reads and the writes
 //                       (without that round trip the same bytes took 5% longer);
+//                       four units per wave as the kernel, or two (finer
+//                       waves, which the same bytes stream faster with);
 //   * stream_empty    - a launch that does nothing: the fixed cost of one
 //                       launch on a stream.
 // Every kernel covers exactly `rows` rows; the host sizes the grid so that no
@@ -89,40 +91,46 @@ __global__ __launch_bounds__(256) void stream_write(uint8_t* dst, uint64_t rows,
 
 // Per unit u: read the 1 KiB row u of src; write 512 bytes at codes + 512 u
 // (nontemporal) and 16 bytes at scales + 16 u (plain), as inv_rope_fp8_quant
-// does with group-major outputs.  Four units per wave; lanes 0..31 write units
-// 0 and 2, lanes 32..63 units 1 and 3, 16 bytes each.
+// does with group-major outputs.  U units per wave (4, as the kernel, or 2);
+// each store instruction writes two units' code rows, lanes 0..31 the even
+// unit and lanes 32..63 the odd one, 16 bytes each.
+template <int U>
 __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* codes,
                                                   uint8_t* scales, uint64_t units) {
   extern __shared__ u32x4_t lds[];
   const uint32_t lane = threadIdx.x & 63;
-  const uint64_t u0 = (uint64_t)wave_id(6) * 4;
-  u32x4_t in[4];
+  const uint64_t u0 = (uint64_t)wave_id(6) * U;
+  u32x4_t in[U];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < U; ++k) {
     const uint64_t u = u0 + k < units ? u0 + k : units - 1;
     in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
   }
-  // through the wave's 4 KiB of LDS and back, lanes permuted, as the kernel's
+  // through the wave's U KiB of LDS and back, lanes permuted, as the kernel's
   // transpose does
-  u32x4_t* slice = lds + 256 * (threadIdx.x >> 6);
+  u32x4_t* slice = lds + 64 * U * (threadIdx.x >> 6);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) slice[64 * k + lane] = in[k];
+  for (int k = 0; k < U; ++k) slice[64 * k + lane] = in[k];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int k = 0; k < 4; ++k) in[k] = slice[64 * k + (lane ^ 5)];
+  for (int k = 0; k < U; ++k) in[k] = slice[64 * k + (lane ^ 5)];
   const uint32_t half = lane >> 5, j = lane & 31;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < U / 2; ++k) {
     const uint64_t u = u0 + 2 * k + half;
     // something from every row read, so no load is dead
     const u32x4_t w = in[2 * k + half] ^ in[2 * k + 1 - half];
     if (u < units) __builtin_nontemporal_store(w, (gptr)(codes + u * 512 + 16 * j));
   }
+  // unit k's scales from lane 16 k
   const uint32_t row = lane >> 4;
-  if ((lane & 15) == 0 && u0 + row < units) {
-    const u32x4_t s = in[row];
+  if ((lane & 15) == 0 && row < (uint32_t)U && u0 + row < units) {
+    u32x4_t s = in[0];
+#pragma unroll
+    for (int k = 1; k < U; ++k)
+      if (row == (uint32_t)k) s = in[k];
     *(gptr)(scales + (u0 + row) * 16) = s;
   }
 }
@@ -156,10 +164,18 @@ int bench_stream_write(void* dst, uint64_t rows, int policy, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units, void* stream) {
+int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units,
+                     int units_per_wave, void* stream) {
   if (units == 0 || units > (1ull << 36)) return -1;
-  hipLaunchKernelGGL(stream_irq, dim3(grid_for(units, 8)), dim3(128), 2 * 4096, (hipStream_t)stream,
-                     (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+  const hipStream_t s = (hipStream_t)stream;
+  if (units_per_wave == 4)
+    hipLaunchKernelGGL(stream_irq<4>, dim3(grid_for(units, 8)), dim3(128), 2 * 4096, s,
+                       (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+  else if (units_per_wave == 2)
+    hipLaunchKernelGGL(stream_irq<2>, dim3(grid_for(units, 4)), dim3(128), 2 * 2048, s,
+                       (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+  else
+    return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
