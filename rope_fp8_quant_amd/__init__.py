@@ -51,12 +51,14 @@ def _cuda(t, name):
 
 
 def _same_device(ref, *named):
+    """Checks that every named tensor is on ref's device; returns its index."""
     # device indices as ints: cheaper than building torch.device objects, and
     # a CPU tensor (index -1) fails too
     d = ref.get_device()
     for t, name in named:
         if t is not None and t.get_device() != d:
             raise ValueError(f"{name} must be on {ref.device}")
+    return d
 
 
 # torch's handle of the current stream of a device and its current device
@@ -130,13 +132,16 @@ def prepare(op, *args, **kwargs):
 
 
 def _check_rope_inputs(positions, cos_sin_cache, n_tokens):
-    if positions.dtype != torch.int64 or positions.dim() != 1 or positions.shape[0] != n_tokens:
+    """Checks positions and the table; returns the table's row count."""
+    if positions.dtype != torch.int64 or positions.shape != (n_tokens,):
         raise ValueError("positions must be int64 [N]")
     if not positions.is_contiguous():
         raise ValueError("positions must be contiguous")
-    if (cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2
-            or cos_sin_cache.shape[1] != 64 or not cos_sin_cache.is_contiguous()):
+    cs_shape = cos_sin_cache.shape
+    if (cos_sin_cache.dtype != torch.float32 or len(cs_shape) != 2 or cs_shape[1] != 64
+            or not cos_sin_cache.is_contiguous()):
         raise ValueError("cos_sin_cache must be contiguous float32 [max_pos, 64]")
+    return cs_shape[0]
 
 
 def abi_version():
@@ -186,10 +191,10 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
     "fp32" or int32/uint32 [G, N, hpg] words for "ue8m0" (any strides).
     """
     fmt = _fmt(scale_fmt)
-    N, H, hpg, G = _check_o(o, heads_per_group)
-    _check_rope_inputs(positions, cos_sin_cache, N)
-    if out.dtype not in _BYTE_DTYPES or out.shape != (G, N, hpg * 512) or (
-            out.stride(2) != 1):
+    N, H, hpg, G, o_st = _check_o(o, heads_per_group)
+    max_pos = _check_rope_inputs(positions, cos_sin_cache, N)
+    out_st = out.stride()
+    if out.dtype not in _BYTE_DTYPES or out.shape != (G, N, hpg * 512) or out_st[2] != 1:
         raise ValueError(f"out must be uint8/float8_e4m3fn [{G}, {N}, {hpg * 512}], last dim "
                          "contiguous")
     if fmt == RQ_SCALE_UE8M0:
@@ -197,24 +202,26 @@ def inv_rope_fp8_quant(o, positions, cos_sin_cache, heads_per_group, out, scales
             raise ValueError(f"ue8m0 scales must be int32/uint32 [{G}, {N}, {hpg}]")
     elif scales.dtype != torch.float32 or scales.shape != (G, N, hpg * 4):
         raise ValueError(f"fp32 scales must be float32 [{G}, {N}, {hpg * 4}]")
-    _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"),
-                 (scales, "scales"))
-    _call("inv_rope_fp8_quant", o.get_device(), stream,
-        o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
-        cos_sin_cache.shape[0], N, H, hpg, fmt, float(eps),
-        out.data_ptr(), out.stride(0), out.stride(1),
-        scales.data_ptr(), scales.stride(0), scales.stride(1), scales.stride(2))
+    idx = _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                       (out, "out"), (scales, "scales"))
+    sc_st = scales.stride()
+    _call("inv_rope_fp8_quant", idx, stream,
+        o.data_ptr(), o_st[0], o_st[1], positions.data_ptr(), cos_sin_cache.data_ptr(),
+        max_pos, N, H, hpg, fmt, float(eps), out.data_ptr(), out_st[0], out_st[1],
+        scales.data_ptr(), sc_st[0], sc_st[1], sc_st[2])
 
 
 def _check_o(o, heads_per_group):
+    """Checks o; returns N, H, heads per group, groups and o's strides."""
     _cuda(o, "o")
-    if o.dtype != torch.bfloat16 or o.dim() != 3 or o.shape[2] != 512 or o.stride(2) != 1:
+    shape, st = o.shape, o.stride()
+    if o.dtype != torch.bfloat16 or len(shape) != 3 or shape[2] != 512 or st[2] != 1:
         raise ValueError("o must be bf16 [N, H, 512] with a contiguous last dim")
-    N, H, _ = o.shape
+    N, H, _ = shape
     hpg = int(heads_per_group)
     if hpg < 1 or H % hpg:
         raise ValueError("heads_per_group must divide the head count")
-    return N, H, hpg, H // hpg
+    return N, H, hpg, H // hpg, st
 
 
 def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None):
@@ -223,31 +230,34 @@ def inv_rope_bf16(o, positions, cos_sin_cache, heads_per_group, out, stream=None
     two dims, last dim contiguous; the token-major view
     ``t.view(N, G, hpg*512).transpose(0, 1)`` of a [N, H, 512] tensor works,
     and that view of o itself rotates o in place)."""
-    N, H, hpg, G = _check_o(o, heads_per_group)
-    _check_rope_inputs(positions, cos_sin_cache, N)
-    if out.dtype != torch.bfloat16 or out.shape != (G, N, hpg * 512) or (
-            out.stride(2) != 1):
+    N, H, hpg, G, o_st = _check_o(o, heads_per_group)
+    max_pos = _check_rope_inputs(positions, cos_sin_cache, N)
+    out_st = out.stride()
+    if out.dtype != torch.bfloat16 or out.shape != (G, N, hpg * 512) or out_st[2] != 1:
         raise ValueError(f"out must be bf16 [{G}, {N}, {hpg * 512}], last dim contiguous")
-    _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"), (out, "out"))
-    _call("inv_rope_bf16", o.get_device(), stream,
-        o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(), cos_sin_cache.data_ptr(),
-        cos_sin_cache.shape[0], N, H, hpg, out.data_ptr(), out.stride(0), out.stride(1))
+    idx = _same_device(o, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                       (out, "out"))
+    _call("inv_rope_bf16", idx, stream,
+        o.data_ptr(), o_st[0], o_st[1], positions.data_ptr(), cos_sin_cache.data_ptr(),
+        max_pos, N, H, hpg, out.data_ptr(), out_st[0], out_st[1])
 
 
 def _check_q_in(q_in, norm_weight, positions, cos_sin_cache):
+    """Checks q_in, the norm weight and the rope inputs; returns N, Hq,
+    q_in's strides, the table's row count and the device index."""
     _cuda(q_in, "q_in")
-    if q_in.dtype != torch.bfloat16 or q_in.dim() != 3 or q_in.shape[2] != 512 or (
-            q_in.stride(2) != 1):
+    shape, st = q_in.shape, q_in.stride()
+    if q_in.dtype != torch.bfloat16 or len(shape) != 3 or shape[2] != 512 or st[2] != 1:
         raise ValueError("q_in must be bf16 [N, Hq, 512] with a contiguous last dim")
-    N, Hq, _ = q_in.shape
-    _check_rope_inputs(positions, cos_sin_cache, N)
+    N, Hq, _ = shape
+    max_pos = _check_rope_inputs(positions, cos_sin_cache, N)
     if norm_weight is not None and (norm_weight.dtype != torch.bfloat16
                                     or norm_weight.shape != (512,)
                                     or not norm_weight.is_contiguous()):
         raise ValueError("norm_weight must be contiguous bf16 [512] or None")
-    _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
-                 (norm_weight, "norm_weight"))
-    return N, Hq
+    idx = _same_device(q_in, (positions, "positions"), (cos_sin_cache, "cos_sin_cache"),
+                       (norm_weight, "norm_weight"))
+    return N, Hq, st, max_pos, idx
 
 
 def _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq):
@@ -269,14 +279,17 @@ def _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq):
 
 
 def _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out):
-    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
-    if (q_out.dtype != q_in.dtype or q_out.dim() != 3 or q_out.shape[0] != N
-            or q_out.shape[2] != 512 or not q_out.is_contiguous()):
+    """_check_q_in and q_out; returns N, Hq, q_head_padded, q_in's strides,
+    the table's row count and the device index."""
+    N, Hq, st, max_pos, idx = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    shape = q_out.shape
+    if (q_out.dtype != q_in.dtype or len(shape) != 3 or shape[0] != N or shape[2] != 512
+            or not q_out.is_contiguous()):
         raise ValueError("q_out must be contiguous bf16 [N, q_head_padded, 512]")
-    if q_out.shape[1] < Hq:
+    if shape[1] < Hq:
         raise ValueError("q_head_padded must be >= num_heads_q")
     _same_device(q_in, (q_out, "q_out"))
-    return N, Hq
+    return N, Hq, shape[1], st, max_pos, idx
 
 
 def _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size):
@@ -319,11 +332,11 @@ def qnorm_rope(q_in, norm_weight, positions, cos_sin_cache, q_out, eps=1e-6, str
     contiguous q_out [N, q_head_padded, 512] bf16; pad heads are zeroed.
     norm_weight: bf16 [512] or None.  With q_head_padded == Hq, q_out may be
     q_in itself (contiguous): each head is read before it is written."""
-    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
-    _call("qnorm_rope", q_in.get_device(), stream,
-        q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
-        None if norm_weight is None else norm_weight.data_ptr(), positions.data_ptr(),
-        cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], N, Hq, q_out.shape[1], float(eps),
+    N, Hq, hpad, st, max_pos, idx = _check_qnr(q_in, norm_weight, positions, cos_sin_cache,
+                                               q_out)
+    _call("qnorm_rope", idx, stream,
+        q_in.data_ptr(), st[0], st[1], None if norm_weight is None else norm_weight.data_ptr(),
+        positions.data_ptr(), cos_sin_cache.data_ptr(), max_pos, N, Hq, hpad, float(eps),
         q_out.data_ptr())
 
 
@@ -333,7 +346,7 @@ def qnorm_rope_fp8(q_in, norm_weight, positions, cos_sin_cache, q_fp8, q_scales,
     [N, q_head_padded, 512] and scales q_scales (float32 [N, Hpad, 4], or
     int32/uint32 [N, Hpad] UE8M0 words); pad heads are quantized zero heads."""
     fmt = _fmt(scale_fmt)
-    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    N, Hq, _, _, _ = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
     _call("qnorm_rope_fp8", q_in.get_device(), stream,
         q_in.data_ptr(), q_in.stride(0), q_in.stride(1),
@@ -371,7 +384,7 @@ def qnorm_rope_kv_rope_quant_insert(q_in, norm_weight, kv, positions, cos_sin_ca
                                     scale_fmt="fp32", quant_eps=1e-10, stream=None):
     """qnorm_rope and kv_rope_quant_insert in one launch (same results)."""
     fmt = _fmt(scale_fmt)
-    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
+    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)[:2]
     if _check_kvi(kv, positions, cos_sin_cache, slot_mapping, k_cache, cache_block_size) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
     _call("qnorm_rope_kv_rope_quant_insert", q_in.get_device(), stream,
@@ -387,7 +400,7 @@ def qnorm_rope_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin_cac
                                    slot_mapping, q_out, cache, eps=1e-6, stream=None):
     """Full-cache form of the fused op in one launch: qnorm_rope (q_out may be
     q_in itself) and kv_rope_insert_full."""
-    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)
+    N, Hq = _check_qnr(q_in, norm_weight, positions, cos_sin_cache, q_out)[:2]
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
     _call("qnorm_rope_kv_rope_insert_full", q_in.get_device(), stream,
@@ -404,7 +417,7 @@ def qnorm_rope_fp8_kv_rope_insert_full(q_in, norm_weight, kv, positions, cos_sin
     """Full-cache form of the fused op with q to FP8, in one launch:
     qnorm_rope_fp8 and kv_rope_insert_full."""
     fmt = _fmt(scale_fmt)
-    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)
+    N, Hq = _check_q_in(q_in, norm_weight, positions, cos_sin_cache)[:2]
     hpad = _check_q_fp8(q_in, q_fp8, q_scales, fmt, N, Hq)
     if _check_kvf(kv, positions, cos_sin_cache, slot_mapping, cache) != N:
         raise ValueError("q_in and kv must have the same number of tokens")
