@@ -869,7 +869,7 @@ def write_counters_json(irq_fetch, irq_write, copy_fetch, copy_write, sq=None):
     from rope_fp8_quant_amd import synth
     cfg = synth.IRQ_PREFILL
     N, H = cfg["N"], cfg["H"]
-    grid = N * H * 16  # 16 threads per unit
+    grid = N * H * 32  # 64 threads per two units
 
     def pick(path, kernel, counter, grid_size=None):
         for (k, g, c), (v, _) in counter_medians(path).items():

@@ -11,12 +11,12 @@
 //                       wave (timed fastest of 4, 8 and 16);
 //   * stream_irq      - inv_rope_fp8_quant's traffic per 512-dim unit: a 1 KiB
 //                       row read, 512 bytes and one 16-byte scale group
-//                       written, with the kernel's workgroup size (128
-//                       threads), XCD chunking (64 workgroups) and its round
-//                       trip through LDS between the reads and the writes
-//                       (without that round trip the same bytes took 5% longer);
-//                       four units per wave as the kernel, or two (finer
-//                       waves, which the same bytes stream faster with);
+//                       written, in 128-thread workgroups dealt to the XCDs
+//                       in chunks of 64, with a round trip through LDS
+//                       between the reads and the writes as the kernels make
+//                       (without it the same bytes took 5% longer); four
+//                       units per wave (the library's common structure) or
+//                       two (inv_rope_fp8_quant's);
 //   * stream_empty    - a launch that does nothing: the fixed cost of one
 //                       launch on a stream.
 // Every kernel covers exactly `rows` rows; the host sizes the grid so that no

@@ -38,9 +38,9 @@
  *     NULL = the default stream) and the call returns without waiting.
  *   - Launch shape: a fixed table picks the workgroup size from the size of
  *     the call alone (the analogue of [P4] section 4's program-count rule):
- *     calls of at least 16384 512-dim units (indexer: 8192 4-head items) use
- *     128-thread workgroups for inv_rope_fp8_quant and 256 for the others,
- *     smaller calls 64.  Results never depend on the entry taken.
+ *     calls of at least 16384 512-dim units (indexer: 16384 4-head items)
+ *     use 256-thread workgroups, smaller calls 64.  Results never depend on
+ *     the entry taken.
  *   - Return value: RQ_OK (0) or a negative RQ_ERR_* status.  On any error
  *     nothing is launched and no output byte is touched.  n_tokens == 0
  *     returns RQ_OK with no launch (pointers are then not inspected).

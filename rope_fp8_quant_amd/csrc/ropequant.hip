@@ -96,9 +96,7 @@ constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
 constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within the row
-constexpr int kRowShl4 = 0x104;       // lane i <- lane i+4 within the row
 constexpr int kRowShl8 = 0x108;       // lane i <- lane i+8 within the row
-constexpr int kRowShl12 = 0x10C;      // lane i <- lane i+12 within the row
 
 // Every control used here either has a source lane for each lane or leaves
 // the lanes without one at 0, so bound_ctrl (write 0) and an old value of 0
@@ -260,6 +258,31 @@ __device__ __forceinline__ void rope_lane(Vals& v, const RopeCS& cs) {
   }
 }
 
+// The scale of a block whose absolute maximum is m ([P4] section 3): m is
+// floored at eps; FP32 mode gives scale = m/448 and the multiplier 1/scale,
+// both correctly rounded; UE8M0 gives scale = 2^k for the smallest k with
+// m/448 <= 2^k, the multiplier 2^-k and the exponent byte k+127.  An
+// infinite m (a rotated pair past the fp32 range) gives scale +inf with
+// multiplier 0 (FP32), or k = 128 (UE8M0).
+template <int FMT>
+__device__ __forceinline__ void block_scale(float m, float eps, float& scale, float& mult,
+                                            uint32_t& ebyte) {
+  m = __builtin_fmaxf(m, eps);
+  if (FMT == RQ_SCALE_UE8M0) {
+    const float t = m < __builtin_inff() ? div448(m) : m;
+    const uint32_t u = __builtin_bit_cast(uint32_t, t);
+    const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
+    scale = pow2_f32(kexp);
+    mult = pow2_neg_f32(kexp);
+    ebyte = (uint32_t)(kexp + 127);
+  } else {
+    const bool finite = m < __builtin_inff();
+    scale = finite ? div448(m) : m;
+    mult = finite ? recip_scale(scale) : 0.0f;
+    ebyte = 0;
+  }
+}
+
 // Block quantization of the lane's 32 values ([P4] section 3).  The 4 lanes
 // of a quad share block q.  Returns the block's scale value (FP32 mode:
 // m/448; UE8M0: 2^k) and the exponent byte k+127 (UE8M0), and the codes as
@@ -274,21 +297,8 @@ __device__ __forceinline__ void quantize_lane(const Vals& v, float eps, float& s
     for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v.x[k][e]));
   m = max_dpp_nonneg<kQuadSwap1>(m);
   m = max_dpp_nonneg<kQuadSwap2>(m);
-  m = __builtin_fmaxf(m, eps);
   float mult;
-  if (FMT == RQ_SCALE_UE8M0) {
-    const float t = m < __builtin_inff() ? div448(m) : m;
-    const uint32_t u = __builtin_bit_cast(uint32_t, t);
-    const int kexp = (int)((u >> 23) & 0xFFu) - 127 + ((u & 0x7FFFFFu) ? 1 : 0);
-    scale = pow2_f32(kexp);
-    mult = pow2_neg_f32(kexp);
-    ebyte = (uint32_t)(kexp + 127);
-  } else {
-    const bool finite = m < __builtin_inff();
-    scale = finite ? div448(m) : m;
-    mult = finite ? recip_scale(scale) : 0.0f;
-    ebyte = 0;
-  }
+  block_scale<FMT>(m, eps, scale, mult, ebyte);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -477,14 +487,15 @@ __device__ __forceinline__ T pick_row(int q, T v0, T v1, T v2, T v3) {
 }
 #define PICK_ROW(q, a) pick_row((q), (a)[0], (a)[1], (a)[2], (a)[3])
 
-// OUT: RQ_SCALE_FP32 / RQ_SCALE_UE8M0 (codes and scales), or kOutBf16 (the
-// rotation only, bf16 rows in the same group-major places).
-template <int OUT>
-__global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
-  constexpr bool kBf16 = OUT == kOutBf16;
+// inv_rope_bf16: the rotation only, bf16 rows in inv_rope_fp8_quant's
+// group-major places (quantization off).  Four units per wave, in the common
+// structure: a 16-lane row per unit, its 32 dims per lane through the LDS
+// transpose, the rows staged back through LDS for whole-row stores.  (The
+// two-unit structure of irq_kernel below measured 0.5% slower here.)
+__global__ __launch_bounds__(256) void irb_kernel(IrqParams p) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
+  const int q = lane >> 4, L = lane & 15, r = L & 3;
   const uint32_t unit0 = wave_index(p.hdr) * 4u;
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   // The wave's four units, all wave-uniform (scalar registers and loads).
@@ -495,7 +506,6 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   int64_t posk[4];
   uint32_t badk[4];
   uint8_t* outk[4];
-  uint8_t* sck[4];  // the unit's first scale
   bool ok[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -506,11 +516,7 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
     const uint32_t j = h - g * p.hpg;
     rows[k] = p.o + (int64_t)t * p.o_st + (int64_t)h * p.o_sh;
     posk[k] = load_uniform(p.positions + t);
-    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st +
-              (int64_t)j * (kBf16 ? 2 * kHeadDim : kHeadDim);
-    const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
-                          (int64_t)(OUT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
-    sck[k] = static_cast<uint8_t*>(p.scales) + 4 * first;
+    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * 2 * kHeadDim;
     ok[k] = unit0 + k < p.units;
   }
   uint4 raw[4], w[4];
@@ -532,52 +538,177 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   Vals v;
   unpack_bf16(w, v);
   if (L >= 12) rope_lane<true>(v, cs);
-
-  if constexpr (kBf16) {
-    // a unit whose position is outside the table is written as NaN
-    uint4 outv[4];
-    pack_bf16(v, outv);
-    if (PICK_ROW(q, badk) != 0) {
+  // a unit whose position is outside the table is written as NaN
+  uint4 outv[4];
+  pack_bf16(v, outv);
+  if (PICK_ROW(q, badk) != 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    }
-    store_rows_bf16<kStoreNt>(lds_wave, outv, lane, outk, ok);
-  } else {
-    float scale;
-    uint32_t ebyte, codes[8];
-    quantize_lane<OUT>(v, p.eps, scale, ebyte, codes);
+    for (int k = 0; k < 4; ++k)
+      outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+  }
+  store_rows_bf16<kStoreNt>(lds_wave, outv, lane, outk, ok);
+}
 
-    // scales.  A unit whose position is outside the table gets NaN scales,
-    // which turns all of its dequantized values into NaN.  FP32 scales laid
-    // out four to a head (the group-major and token-major layouts) are
-    // gathered into the row's first lane and written with one 16-byte
-    // store: the per-block 4-byte stores of 16 lanes measured 3.5% slower
-    // over the whole kernel, and a nontemporal 16-byte store 1% slower.
-    // Other layouts (MN-major) take one 4-byte store per block.
-    if (unit0 + q < p.units) {
-      const bool bad = PICK_ROW(q, badk) != 0;
-      uint8_t* sc = PICK_ROW(q, sck);
-      if (OUT == RQ_SCALE_UE8M0) {
-        const uint32_t word = pack_ue8m0(ebyte, blk);
-        if (L == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
-      } else {
-        const float sv = bad ? __builtin_nanf("") : scale;
-        if (p.sc_vec4) {
-          // block b's scale sits in quad b: lanes 4, 8, 12 of the row
-          const float s1 = dpp_f32<kRowShl4>(sv);
-          const float s2 = dpp_f32<kRowShl8>(sv);
-          const float s3 = dpp_f32<kRowShl12>(sv);
-          if (L == 0)
-            *reinterpret_cast<uint4*>(sc) =
-                make_uint4(__builtin_bit_cast(uint32_t, sv), __builtin_bit_cast(uint32_t, s1),
-                           __builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, s3));
-        } else if (r == 0) {
-          reinterpret_cast<float*>(sc)[(int64_t)blk * p.sc_sb] = sv;
-        }
+// inv_rope_fp8_quant, two units per wave: lanes 32h .. 32h+31 work on unit h
+// of the wave.  Within a half, lane L = 8b + r holds the 8-dim chunks 16b + r
+// and 16b + 8 + r of its unit, so quant block b is the aligned 8-lane group
+// b (three DPP steps for its maximum) and the rotated dims 448..511 are the
+// second chunks of group 3, one chunk (4 GPT-J pairs, 4r .. 4r+3) per lane.
+// Each unit's 1 KiB row is read by one 16-byte-per-lane load and reaches
+// those lanes through the wave's 2 KiB of LDS; 16-byte slot s sits at
+// s ^ (((s >> 4) & 1) << 3), and 8-byte code granule G at
+// G ^ (((G >> 5) & 1) << 3), which keeps every LDS access free of bank
+// conflicts.  One store instruction writes both units' 512-byte code rows
+// (lanes 0..31 unit 0, 32..63 unit 1).
+//
+// Why two units per wave: the same bytes streamed with no arithmetic took
+// 120.9 us with 2 KiB per wave against 126.0 us with 4 KiB for the 16384 x 32
+// workload on MI355X.  The four-unit form of this kernel (a 16-lane row per
+// unit) ran at the latter; this one, in 256-thread workgroups dealt to the
+// XCDs in chunks of 64, runs at 122.5-123.0 us, and 2-3% faster on the
+// irregular and larger launches.  Waves of one unit, or two in a layout
+// without the transpose, were slower than both: their rotation and scale
+// work falls on fewer lanes.
+template <int FMT>
+__global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, L = lane & 31, b = L >> 3, r = L & 7;
+  const uint32_t unit0 = wave_index(p.hdr) * 2u;
+  uint4* lds_wave = lds + 128 * (threadIdx.x >> 6);
+  const uint16_t* rows[2];
+  const float* csk[2];
+  int64_t posk[2];
+  uint32_t badk[2];
+  uint8_t* outk[2];
+  uint8_t* sck[2];
+  bool ok[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t u = min(unit0 + k, p.units - 1u);
+    const uint32_t t = magic_div(u, p.div_heads);
+    const uint32_t hh = u - t * p.n_heads;
+    const uint32_t g = magic_div(hh, p.div_hpg);
+    const uint32_t j = hh - g * p.hpg;
+    rows[k] = p.o + (int64_t)t * p.o_st + (int64_t)hh * p.o_sh;
+    posk[k] = load_uniform(p.positions + t);
+    outk[k] = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim;
+    const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                          (int64_t)(FMT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
+    sck[k] = static_cast<uint8_t*>(p.scales) + 4 * first;
+    ok[k] = unit0 + k < p.units;
+  }
+  uint4 raw[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
+    badk[k] = bad;
+    csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+  }
+  // cos / sin of the lane's 4 pairs 4r .. 4r+3 (used by group 3 only; read
+  // by every lane, cached)
+  const float4* csrow = reinterpret_cast<const float4*>(h ? csk[1] : csk[0]);
+  const float4 c4 = csrow[r], s4 = csrow[8 + r];
+  const bool row_bad = (h ? badk[1] : badk[0]) != 0;
+
+  // transpose: slot s of unit k at 64k + (s ^ (((s >> 4) & 1) << 3))
+#pragma unroll
+  for (int k = 0; k < 2; ++k) lds_wave[64 * k + (lane ^ (((lane >> 4) & 1) << 3))] = raw[k];
+  wave_lds_sync();
+  const int c0 = 16 * b + r, c1 = 16 * b + 8 + r;
+  const uint4 w0 = lds_wave[64 * h + (c0 ^ (((c0 >> 4) & 1) << 3))];
+  const uint4 w1 = lds_wave[64 * h + (c1 ^ (((c1 >> 4) & 1) << 3))];
+
+  float x[2][8];
+  {
+    const uint32_t d0[4] = {w0.x, w0.y, w0.z, w0.w}, d1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[0][2 * i] = bf_lo(d0[i]);
+      x[0][2 * i + 1] = bf_hi(d0[i]);
+      x[1][2 * i] = bf_lo(d1[i]);
+      x[1][2 * i + 1] = bf_hi(d1[i]);
+    }
+  }
+  if (b == 3) {
+    // inverse GPT-J rotation ([P4] section 2): e' = e*c + o*s, o' = o*c - e*s
+    const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = x[1][2 * i], o = x[1][2 * i + 1];
+      const float ec = e * cv[i], os = o * sv[i], oc = o * cv[i], es = e * sv[i];
+      x[1][2 * i] = ec + os;
+      x[1][2 * i + 1] = oc - es;
+    }
+  }
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+
+  {
+    // block amax over the 8-lane group ([P4] section 3)
+    float m = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[cc][e]));
+    m = max_dpp_nonneg<kQuadSwap1>(m);
+    m = max_dpp_nonneg<kQuadSwap2>(m);
+    m = max_dpp_nonneg<kRowHalfMirror>(m);
+    float scale, mult;
+    uint32_t ebyte;
+    block_scale<FMT>(m, p.eps, scale, mult, ebyte);
+    // No clamp before the convert: |x * mult| <= 448 * (1 + 2^-24)^3, and
+    // the convert rounds to nearest even, giving 448 up to 464.
+    uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      uint32_t code[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float q0 = x[cc][4 * hf] * mult, q1 = x[cc][4 * hf + 1] * mult;
+        const float q2 = x[cc][4 * hf + 2] * mult, q3 = x[cc][4 * hf + 3] * mult;
+        // bytes 2..3 of the first convert are overwritten by the second
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, __builtin_bit_cast(int, q0), false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, wd, true);
+        code[hf] = (uint32_t)wd;
+      }
+      const int G = cc ? c1 : c0;  // 8-byte granule of the unit's code row
+      lds8[64 * h + (G ^ (((G >> 5) & 1) << 3))] = make_uint2(code[0], code[1]);
+    }
+
+    // scales.  A unit whose position is outside the table gets NaN scales.
+    // Block b's value is uniform over group b.  Lane 32h gathers its unit's
+    // four (group 1 through a DPP row shift, groups 2 and 3 from lane
+    // 32h + 16 through ds_bpermute) and writes them with one 16-byte store
+    // when they are contiguous and aligned; else the first lane of each
+    // group writes its own (MN-major layouts).
+    uint8_t* const sc = h ? sck[1] : sck[0];
+    const bool sc_ok = h ? ok[1] : ok[0];
+    if (FMT == RQ_SCALE_UE8M0) {
+      uint32_t wd = ebyte << (8 * b);
+      wd |= dpp_u32<kRowMirror>(wd);  // the row's other group
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)wd);
+      if (L == 0 && sc_ok) *reinterpret_cast<uint32_t*>(sc) = row_bad ? 0xFFFFFFFFu : (wd | hi);
+    } else {
+      const float sv = row_bad ? __builtin_nanf("") : scale;
+      if (p.sc_vec4) {
+        const uint32_t s0 = __builtin_bit_cast(uint32_t, sv);
+        const uint32_t s1 = dpp_u32<kRowShl8>(s0);
+        const uint32_t s2 = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)s0);
+        const uint32_t s3 = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)s1);
+        if (L == 0 && sc_ok) *reinterpret_cast<uint4*>(sc) = make_uint4(s0, s1, s2, s3);
+      } else if (r == 0 && sc_ok) {
+        reinterpret_cast<float*>(sc)[(int64_t)b * p.sc_sb] = sv;
       }
     }
-    store_rows_fp8<kStoreNt>(lds_wave, codes, lane, outk, unit0, p.units);
+    wave_lds_sync();
+    // codes: lane (h, j) stores bytes 16j .. 16j+15 of unit h's row; one
+    // instruction writes both units' rows (two half-wave stores through
+    // scalar bases measured 1.2% slower)
+    const int G0 = 2 * L;
+    const uint4 cw = *reinterpret_cast<const uint4*>(lds8 + 64 * h + (G0 ^ (((G0 >> 5) & 1) << 3)));
+    if (h ? ok[1] : ok[0]) store_nt((h ? outk[1] : outk[0]) + 16 * L, cw);
   }
 }
 
@@ -829,7 +960,7 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // slots and positions used only now (see irq_kernel)
+  for (int k = 0; k < 4; ++k) {  // slots and positions used only now (see irb_kernel)
     const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
     badk[k] = bad;
     csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
@@ -1129,10 +1260,10 @@ struct LaunchShape {
 };
 
 // Launch table: the analogue of [P4] section 4's program-count rule.  Many
-// units (prefill): the kernel's prefill workgroup size (128 or 256 threads,
-// 8 or 16 units), plenty of workgroups per CU.  Few units (decode): 64-thread
-// workgroups (4 units) so the work spreads over as many CUs as possible.
-// Results do not depend on the choice.
+// units (prefill): the kernel's prefill workgroup size (256 threads for
+// every kernel now), plenty of workgroups per CU.  Few units (decode):
+// 64-thread workgroups, one wave each, so the work spreads over as many CUs
+// as possible.  Results do not depend on the choice.
 int pick_block_threads(uint32_t units, int prefill_threads) {
   return units >= 16384u ? prefill_threads : 64;
 }
@@ -1187,23 +1318,26 @@ bool extent_ok(int nd, const int64_t* n, const int64_t* s, int64_t row, int64_t 
 }
 
 // Every params struct starts with a LaunchHdr, filled in here.
+// `units` counts the kernel's work units (512-dim heads; the indexer's
+// 4-head items), `units_per_wave` how many one wave takes (4, or 2 for
+// inv_rope_fp8_quant).  Each wave gets 1 KiB of LDS per unit.
 int launch(const void* fn, uint32_t units, LaunchShape shape, void* params,
-           hipStream_t stream, bool uses_lds = true) {
+           hipStream_t stream, uint32_t units_per_wave = 4) {
   const int threads = pick_block_threads(units, shape.prefill_threads);
   LaunchHdr* hdr = static_cast<LaunchHdr*>(params);
   hdr->wpb_log2 = threads == 256 ? 2u : threads == 128 ? 1u : 0u;
   hdr->chunk_log2 = shape.chunk_log2;
-  const uint32_t per_block = (uint32_t)threads / 16u;
+  const uint32_t per_block = (uint32_t)threads / 64u * units_per_wave;
   const uint32_t blocks = (units + per_block - 1) / per_block;
   void* args[] = {params};
-  const size_t lds_bytes = uses_lds ? (size_t)(threads / 64) * 4096 : 0;  // 4 KiB per wave
+  const size_t lds_bytes = (size_t)(threads / 64) * 1024 * units_per_wave;
   const hipError_t e =
       hipLaunchKernel(fn, dim3(blocks), dim3((uint32_t)threads), args, lds_bytes, stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 // Timed with every launch on buffers that earlier launches have not touched.
-constexpr LaunchShape kIrqShape{6, 128};  // FP8 codes
+constexpr LaunchShape kIrqShape{6, 256};  // FP8 codes, two units per wave
 constexpr LaunchShape kIrbShape{6, 256};  // bf16 rows
 constexpr LaunchShape kQnrShape{4, 256};  // bf16 q_out
 constexpr LaunchShape kQf8Shape{4, 256};  // FP8 q_out
@@ -1284,7 +1418,7 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
               sc_stride_token % 4 == 0 && aligned(scales, 16);
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)irq_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.units, kIrqShape, &p, (hipStream_t)stream);
+  return launch(fn, p.units, kIrqShape, &p, (hipStream_t)stream, 2);
 }
 
 int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_head,
@@ -1327,7 +1461,7 @@ int inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_stride_he
   p.out = reinterpret_cast<uint8_t*>(out);
   p.out_sg = 2 * out_stride_group; p.out_st = 2 * out_stride_token;  // bytes in the kernel
   p.scales = nullptr; p.sc_sg = p.sc_st = p.sc_sb = 0; p.sc_vec4 = 0;
-  return launch((const void*)irq_kernel<kOutBf16>, p.units, kIrbShape, &p,
+  return launch((const void*)irb_kernel, p.units, kIrbShape, &p,
                 (hipStream_t)stream);
 }
 

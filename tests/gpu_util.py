@@ -21,17 +21,17 @@ from tests.helpers import e4m3_ulp, torch_e4m3_decode
 
 DEV = "cuda:0"
 
-# The library's launch table: a launch of at least TABLE_ROWS 16-lane rows
-# (one 512-dim unit each; the indexer counts four rows per wave) takes its
-# kernel's prefill workgroup size, a smaller one 64-thread workgroups.  Tests
-# reach both entries by the size of their inputs.
+# The library's launch table: a launch of at least TABLE_ROWS work units
+# (512-dim heads; for the indexer, four-head items: ceil(H/4) per token)
+# takes its kernel's prefill workgroup size, a smaller one 64-thread
+# workgroups.  Tests reach both entries by the size of their inputs.
 TABLE_ROWS = 16384
 SHAPES = ("decode_table", "prefill_table")
 
 
 def table_tokens(shape, rows_per_token, base=37):
     """A token count whose launch lands in table entry `shape`: `base` for the
-    64-thread entry, else past TABLE_ROWS rows.  Where the row count per token
+    64-thread entry, else past TABLE_ROWS units (`rows_per_token` per token).  Where the row count per token
     allows it, the total is kept off a multiple of 16 so that the last
     workgroup is ragged in either entry."""
     if shape == "decode_table":

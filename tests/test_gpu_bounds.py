@@ -138,7 +138,7 @@ def test_kv_paths_tail_waves_write_nothing(shape):
 def test_indexer_tail_waves_write_nothing(shape):
     # 5 heads: two 4-head items per token, the second holding one head; four
     # rows per wave of two items, so 4 rows per token
-    N, H = table_tokens(shape, 4), 5
+    N, H = table_tokens(shape, 2), 5  # ceil(5/4) four-head items per token
     q = synth.normal_bf16((N, H, 128), 155, synth.T_Q)
     w = np.random.default_rng([155, 9]).uniform(0, 1, (N, H)).astype(np.float32)
     pos = synth.uniform_positions(N, 4096, 155)

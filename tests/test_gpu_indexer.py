@@ -6,8 +6,8 @@ import torch
 import oracle
 import rope_fp8_quant_amd as rq
 from rope_fp8_quant_amd import synth
-from tests.gpu_util import (DEV, SHAPES, assert_bits_equal, assert_codes_match, dev, host,
-                            table_tokens)
+from tests.gpu_util import (DEV, SHAPES, TABLE_ROWS, assert_bits_equal, assert_codes_match, dev,
+                            host, table_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_indexer_full_size():
 # rows of the launch table.
 @pytest.mark.parametrize("shape", SHAPES)
 def test_indexer_ragged(shape):
-    idx_check(*idx_inputs(table_tokens(shape, 4), 5, 56, max_pos=65536), f"ragged {shape}")
+    idx_check(*idx_inputs(table_tokens(shape, 2), 5, 56, max_pos=65536), f"ragged {shape}")
 
 
 @pytest.mark.parametrize("N", synth.DECODE_NS)
@@ -75,7 +75,7 @@ def test_indexer_strided_outputs_partial_item(shape):
     # 7 heads: every token's second 4-head item holds 3 heads.  Codes rows
     # padded to 192 bytes, weight rows to 10 and 12 floats; the padding must
     # come back untouched.
-    N, H = table_tokens(shape, 4, base=41), 7
+    N, H = table_tokens(shape, 2, base=41), 7
     q, w, pos, cache = idx_inputs(N, H, 62, max_pos=65536)
     q8_big = torch.full((N, H, 192), 0xCD, dtype=torch.uint8, device=DEV)
     w_big = torch.full((N, 10), -7.0, dtype=torch.float32, device=DEV)
@@ -147,13 +147,14 @@ def test_indexer_bad_position_gives_nan_weight():
 
 
 def test_indexer_launch_table_entries_bit_identical():
-    # 613 tokens x 64 heads (32 rows each) take the prefill entry of the
-    # launch table; the same tokens in two calls of under 512 tokens take the
-    # 64-thread entry
-    q, w, pos, cache = idx_inputs(613, 64, 61, max_pos=65536)
+    # 1031 tokens x 64 heads (16 four-head items each, 16496 in all) take the
+    # prefill entry of the launch table; the same tokens in two calls of
+    # under 1024 tokens take the 64-thread entry
+    q, w, pos, cache = idx_inputs(1031, 64, 61, max_pos=65536)
+    assert 1031 * 16 >= TABLE_ROWS > 516 * 16
     print("[case] indexer launch-table entries", flush=True)
     full, fw = idx_gpu(q, w, pos, cache)
-    for t0, t1 in ((0, 307), (307, 613)):
+    for t0, t1 in ((0, 515), (515, 1031)):
         part, pw = idx_gpu(q[t0:t1].copy(), w[t0:t1].copy(), pos[t0:t1].copy(), cache)
         assert (part == full[t0:t1]).all()
         assert (pw.view(np.uint32) == fw[t0:t1].view(np.uint32)).all()
