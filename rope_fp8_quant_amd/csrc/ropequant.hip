@@ -1030,6 +1030,134 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
   kvi_body<OUT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
 }
 
+// kv_rope_quant_insert standalone, two tokens per wave: the lane layout of
+// irq_kernel (token h on lanes 32h .. 32h+31, lane 8b + r holding chunks
+// 16b + r and 16b + 8 + r, quant block b on 8-lane group b), the forward
+// rotation, and each token's 528-byte record written as 33 16-byte granules:
+// the codes by lanes 32h .. 32h+31 through LDS, the scale tail by lane 32h.
+// With four tokens per wave (kvi_body, which the fused kernel and the bf16
+// cache use) these launches ran 2-7% slower; for the bf16 cache the
+// two-token form was slower from 8192 tokens on.
+template <int FMT>
+__global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, L = lane & 31, b = L >> 3, r = L & 7;
+  const uint32_t t0 = wave_index(p.hdr) * 2u;
+  uint4* lds_wave = lds + 128 * (threadIdx.x >> 6);
+  const uint16_t* rows[2];
+  const float* csk[2];
+  int64_t posk[2], slotk[2];
+  uint32_t badk[2];
+  uint8_t* reck[2];  // the token's record, or nullptr: nothing to write
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t t = min(t0 + k, p.n_tokens - 1u);
+    slotk[k] = load_uniform(p.slots + t);
+    if (t0 + k >= p.n_tokens) slotk[k] = -1;
+    rows[k] = p.kv + (int64_t)t * p.kv_st;
+    posk[k] = load_uniform(p.positions + t);
+  }
+  uint4 raw[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // slots and positions used only now (see irb_kernel)
+    const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
+    badk[k] = bad;
+    csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+    reck[k] = nullptr;
+    if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
+      const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
+      const uint32_t idx = (uint32_t)slotk[k] - blk_i * p.bs;
+      reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
+    }
+  }
+  const float4* csrow = reinterpret_cast<const float4*>(h ? csk[1] : csk[0]);
+  const float4 c4 = csrow[r], s4 = csrow[8 + r];
+  const bool row_bad = (h ? badk[1] : badk[0]) != 0;
+
+  // transpose: slot s of token k at 64k + (s ^ (((s >> 4) & 1) << 3))
+#pragma unroll
+  for (int k = 0; k < 2; ++k) lds_wave[64 * k + (lane ^ (((lane >> 4) & 1) << 3))] = raw[k];
+  wave_lds_sync();
+  const int c0 = 16 * b + r, c1 = 16 * b + 8 + r;
+  const uint4 w0 = lds_wave[64 * h + (c0 ^ (((c0 >> 4) & 1) << 3))];
+  const uint4 w1 = lds_wave[64 * h + (c1 ^ (((c1 >> 4) & 1) << 3))];
+  float x[2][8];
+  {
+    const uint32_t d0[4] = {w0.x, w0.y, w0.z, w0.w}, d1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[0][2 * i] = bf_lo(d0[i]);
+      x[0][2 * i + 1] = bf_hi(d0[i]);
+      x[1][2 * i] = bf_lo(d1[i]);
+      x[1][2 * i + 1] = bf_hi(d1[i]);
+    }
+  }
+  if (b == 3) {
+    // forward GPT-J rotation: e' = e*c - o*s, o' = o*c + e*s
+    const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = x[1][2 * i], o = x[1][2 * i + 1];
+      const float ec = e * cv[i], os = o * sv[i], oc = o * cv[i], es = e * sv[i];
+      x[1][2 * i] = ec - os;
+      x[1][2 * i + 1] = oc + es;
+    }
+  }
+  wave_lds_sync();  // the transpose reads are done before the slice is reused
+  float m = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[cc][e]));
+  m = max_dpp_nonneg<kQuadSwap1>(m);
+  m = max_dpp_nonneg<kQuadSwap2>(m);
+  m = max_dpp_nonneg<kRowHalfMirror>(m);
+  float scale, mult;
+  uint32_t ebyte;
+  block_scale<FMT>(m, p.eps, scale, mult, ebyte);
+  uint2* lds8 = reinterpret_cast<uint2*>(lds_wave);
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    uint32_t code[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const float q0 = x[cc][4 * hf] * mult, q1 = x[cc][4 * hf + 1] * mult;
+      const float q2 = x[cc][4 * hf + 2] * mult, q3 = x[cc][4 * hf + 3] * mult;
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, __builtin_bit_cast(int, q0), false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, wd, true);
+      code[hf] = (uint32_t)wd;
+    }
+    const int G = cc ? c1 : c0;
+    lds8[64 * h + (G ^ (((G >> 5) & 1) << 3))] = make_uint2(code[0], code[1]);
+  }
+  // the record's scale tail, gathered into lane 32h (a token whose position
+  // is outside the table gets NaN scales)
+  uint4 tail;
+  if (FMT == RQ_SCALE_UE8M0) {
+    uint32_t wd = ebyte << (8 * b);
+    wd |= dpp_u32<kRowMirror>(wd);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)wd);
+    tail = make_uint4(row_bad ? 0xFFFFFFFFu : (wd | hi), 0u, 0u, 0u);
+  } else {
+    const uint32_t s0 = row_bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
+    const uint32_t s1 = dpp_u32<kRowShl8>(s0);
+    const uint32_t s2 = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)s0);
+    const uint32_t s3 = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane + 16) & 63), (int)s1);
+    tail = make_uint4(s0, s1, s2, s3);
+  }
+  wave_lds_sync();
+  const int G0 = 2 * L;
+  const uint4 cw = *reinterpret_cast<const uint4*>(lds8 + 64 * h + (G0 ^ (((G0 >> 5) & 1) << 3)));
+  uint8_t* const rec = h ? reck[1] : reck[0];
+  if (rec) {
+    *reinterpret_cast<uint4*>(rec + 16 * L) = cw;
+    if (L == 0) *reinterpret_cast<uint4*>(rec + kHeadDim) = tail;
+  }
+}
+
 // The q path and the kv path in one launch ([P1] section 1: the op
 // normalizes and rotates q and inserts the rotated kv in a single kernel;
 // section 2 names the full-cache forms: q as bf16 (in place) or FP8, kv into
@@ -1665,9 +1793,9 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
                           n_tokens, k_cache, num_blocks, block_stride_bytes, cache_block_size,
                           scale_fmt, eps, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi_kernel<RQ_SCALE_UE8M0>
-                                               : (const void*)kvi_kernel<RQ_SCALE_FP32>;
-  return launch(fn, p.n_tokens, kKviShape, &p, (hipStream_t)stream);
+  const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi2_kernel<RQ_SCALE_UE8M0>
+                                               : (const void*)kvi2_kernel<RQ_SCALE_FP32>;
+  return launch(fn, p.n_tokens, kKviShape, &p, (hipStream_t)stream, 2);
 }
 
 int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token, const int64_t* positions,
