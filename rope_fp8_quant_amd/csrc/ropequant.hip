@@ -949,21 +949,32 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
   uint32_t badk[4];
   uint8_t* reck[4];  // the token's record or row, or nullptr: nothing to write
   int64_t slotk[4];
+  // The slot and position loads are issued first and the row reads right
+  // after, with nothing in between that waits for the former (the scheduling
+  // barriers keep it so); the cos/sin reads, which need the positions, go out
+  // before the slot arithmetic.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t t = min(t0 + k, p.n_tokens - 1u);
-    slotk[k] = load_uniform(p.slots + t);
-    if (t0 + k >= p.n_tokens) slotk[k] = -1;
     rows[k] = p.kv + (int64_t)t * p.kv_st;
+    slotk[k] = load_uniform(p.slots + t);
     posk[k] = load_uniform(p.positions + t);
   }
+  __builtin_amdgcn_sched_barrier(0);
   uint4 raw[4], w[4];
   issue_rows(rows, lane, raw);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // slots and positions used only now (see irb_kernel)
+  for (int k = 0; k < 4; ++k) {
     const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
     badk[k] = bad;
     csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+  }
+  RopeCS cs;
+  load_cs(PICK_ROW(q, csk), r, cs);  // every lane, unconditionally (cached)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (t0 + k >= p.n_tokens) slotk[k] = -1;
     reck[k] = nullptr;
     if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
       if (OUT == kOutBf16) {
@@ -975,8 +986,6 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
       }
     }
   }
-  RopeCS cs;
-  load_cs(PICK_ROW(q, csk), r, cs);  // unconditional, as above
   transpose_rows(lds_wave, raw, lane, w);
 
   if constexpr (OUT == kOutBf16) {
@@ -1050,22 +1059,31 @@ __global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
   int64_t posk[2], slotk[2];
   uint32_t badk[2];
   uint8_t* reck[2];  // the token's record, or nullptr: nothing to write
+  // load order as in kvi_body: slots and positions, rows, then cos/sin
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint32_t t = min(t0 + k, p.n_tokens - 1u);
-    slotk[k] = load_uniform(p.slots + t);
-    if (t0 + k >= p.n_tokens) slotk[k] = -1;
     rows[k] = p.kv + (int64_t)t * p.kv_st;
+    slotk[k] = load_uniform(p.slots + t);
     posk[k] = load_uniform(p.positions + t);
   }
+  __builtin_amdgcn_sched_barrier(0);
   uint4 raw[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) raw[k] = load_nt(reinterpret_cast<const uint4*>(rows[k]) + lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {  // slots and positions used only now (see irb_kernel)
+  for (int k = 0; k < 2; ++k) {
     const bool bad = posk[k] < 0 || posk[k] >= p.max_pos;
     badk[k] = bad;
     csk[k] = p.cs + (bad ? 0 : posk[k]) * 64;
+  }
+  const float4* csrow = reinterpret_cast<const float4*>(h ? csk[1] : csk[0]);
+  const float4 c4 = csrow[r], s4 = csrow[8 + r];
+  const bool row_bad = (h ? badk[1] : badk[0]) != 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (t0 + k >= p.n_tokens) slotk[k] = -1;
     reck[k] = nullptr;
     if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
       const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
@@ -1073,9 +1091,6 @@ __global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
       reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
     }
   }
-  const float4* csrow = reinterpret_cast<const float4*>(h ? csk[1] : csk[0]);
-  const float4 c4 = csrow[r], s4 = csrow[8 + r];
-  const bool row_bad = (h ? badk[1] : badk[0]) != 0;
 
   // transpose: slot s of token k at 64k + (s ^ (((s >> 4) & 1) << 3))
 #pragma unroll
@@ -1236,6 +1251,9 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
   // The wave's four items, wave-uniform.  A slot past the last item repeats
   // the last item, and a head past the token's last reads the item's first
   // head: every read stays inside q, and neither stores anything.
+  // Load order: the positions (scalar), the q rows, then the cos/sin rows
+  // and the head weights; the scheduling barriers keep the compiler from
+  // waiting for the positions before the row reads are issued.
   uint32_t tk[4], h0k[4], nvk[4];
   const uint8_t* qk[4];
   int64_t posk[4];
@@ -1249,6 +1267,7 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
     qk[k] = reinterpret_cast<const uint8_t*>(p.q + (int64_t)t * p.q_st + (int64_t)h0k[k] * p.q_sh);
     posk[k] = load_uniform(p.positions + t);
   }
+  __builtin_amdgcn_sched_barrier(0);
   // Reads: instruction k, lane L' -> head L' >> 4 of item k, granule L' & 15.
   const uint32_t lhead = (uint32_t)lane >> 4;
   uint4 raw[4];
@@ -1258,6 +1277,14 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
     const uint32_t off = (lhead < nv ? lhead * (uint32_t)p.q_sh * 2u : 0u) + 16u * (lane & 15);
     raw[k] = load_nt(qk[k] + off);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // The weight of the lane's head, read now so that its latency overlaps the
+  // q reads' instead of following the arithmetic (every lane reads; a head
+  // past the token's last reads the token's last head and stores nothing).
+  const uint32_t nv = PICK_ROW(row, nvk);
+  const bool wlane = sub == 0 && (uint32_t)hh < nv;
+  const uint32_t wt_tok = PICK_ROW(row, tk), wt_head = PICK_ROW(row, h0k) + (uint32_t)hh;
+  const float wv = p.w[(int64_t)wt_tok * p.w_st + min(wt_head, p.n_heads - 1u)];
   const float* csk[4];
   uint32_t badk[4];
 #pragma unroll
@@ -1329,13 +1356,10 @@ __global__ __launch_bounds__(256) void idx_kernel(IdxParams p) {
       code[2 * c + hf] = (uint32_t)wd;
     }
   }
-  // folded weight of the lane's head (lane s == 0 of the quad)
-  const uint32_t nv = PICK_ROW(row, nvk);
-  if (sub == 0 && (uint32_t)hh < nv) {
-    const uint32_t t = PICK_ROW(row, tk), h = PICK_ROW(row, h0k) + (uint32_t)hh;
-    const float wv = p.w[(int64_t)t * p.w_st + h];
+  // folded weight of the lane's head
+  if (wlane) {
     const float fold = ((wv * qs) * p.softmax_scale) * p.head_scale;
-    p.wo[(int64_t)t * p.wo_st + h] = PICK_ROW(row, badk) ? __builtin_nanf("") : fold;
+    p.wo[(int64_t)wt_tok * p.wo_st + wt_head] = PICK_ROW(row, badk) ? __builtin_nanf("") : fold;
   }
   // codes through LDS (the transpose reads are done before the slice is reused)
   wave_lds_sync();
