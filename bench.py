@@ -439,10 +439,23 @@ def bench_qnr_kvi(args, device, stream):
         fns = [lambda x=x, k=k, o=o, c=c: rq.qnorm_rope_kv_rope_quant_insert(
             x, wd, k, pd, cd, sd, o, c, cfg["block_size"], qc["eps"]) for x, k, o, c in rot]
         ms = time_rotating(fns, args.steps, args.warmup, stream)
+        # The same work as two launches back to back, and the one launch with
+        # the slots in token order (records written contiguously instead of
+        # scattered over the cache): what the fusion saves, and what the
+        # scattered record writes cost inside the q stream.
+        fns2 = [lambda x=x, k=k, o=o, c=c: (
+            rq.qnorm_rope(x, wd, pd, cd, o, qc["eps"]),
+            rq.kv_rope_quant_insert(k, pd, cd, sd, c, cfg["block_size"])) for x, k, o, c in rot]
+        ms_sep = time_rotating(fns2, args.steps, args.warmup, stream)
+        sd_seq = to_dev(np.arange(cfg["N"], dtype=np.int64), device)
+        fns3 = [lambda x=x, k=k, o=o, c=c: rq.qnorm_rope_kv_rope_quant_insert(
+            x, wd, k, pd, cd, sd_seq, o, c, cfg["block_size"], qc["eps"]) for x, k, o, c in rot]
+        ms_seq = time_rotating(fns3, args.steps, args.warmup, stream)
         res["qnorm_rope_kv_rope_quant_insert"] = dict(
             workload="qnr_forward + kvi_forward, one launch", us=ms * 1e3, bytes=b,
-            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS, buffer_sets=sets)
-        del qd, rot, fns
+            gbs=b / ms / 1e6, frac=b / ms / 1e6 / HBM_PEAK_GBS, buffer_sets=sets,
+            us_two_launches=ms_sep * 1e3, us_slots_in_token_order=ms_seq * 1e3)
+        del qd, rot, fns, fns2, fns3
     if args.only in (None, "idx"):
         N, H = 4096, 64
         q = synth.normal_bf16((N, H, 128), 55, synth.T_Q)
