@@ -144,6 +144,22 @@ def test_kvi_holes_gaps_and_out_of_range(shape):
               f"holes {shape}", oracle_slots=o_slots)
 
 
+@pytest.mark.parametrize("N", [4095, 4096])
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_kvi_store_policy_threshold(N, scale_fmt):
+    # The library writes records with plain stores below 4096 tokens and
+    # nontemporal ones from 4096 on; both sides of the switch, with holes,
+    # must match the oracle and leave every other byte alone.
+    bs = 64
+    nb = -(-2 * N // bs)
+    kv = synth.normal_bf16((N, 512), 37, synth.T_KV)
+    pos = synth.uniform_positions(N, 65536, 37)
+    slots = synth.slot_permutation(N, nb * bs, 37)
+    slots[[0, N // 2, N - 1]] = -1
+    kvi_check(kv, pos, synth.cos_sin_cache(65536), slots, nb, bs, None, scale_fmt,
+              f"store-policy switch N={N}")
+
+
 def test_kvi_bad_position_poisons_its_record():
     N, nb, bs = 8, 2, 8
     kv = synth.normal_bf16((N, 512), 36, synth.T_KV)
