@@ -934,20 +934,19 @@ struct KviParams {
   float eps;
 };
 
-// The wave with grid-wide index `wave` handles tokens 4*wave .. 4*wave+3.
-// OUT: RQ_SCALE_FP32 / RQ_SCALE_UE8M0 (a 528-byte record in the paged FP8
-// cache), or kOutBf16 (a bf16 row of the token-strided cache: slot s at
-// cache + s * block_stride bytes).
-template <int OUT>
-__device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint4* lds_wave) {
+// kv_rope_insert_full and the full-cache fused forms: the wave with
+// grid-wide index `wave` rotates tokens 4*wave .. 4*wave+3 and writes each as
+// a bf16 row of the token-strided cache (slot s at cache + s * block_stride
+// bytes).  Two tokens per wave measured slower here from 8192 tokens on.
+__device__ __forceinline__ void kvf_body(const KviParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, L = lane & 15, blk = L >> 2, r = L & 3;
+  const int q = lane >> 4, L = lane & 15, r = L & 3;
   const uint32_t t0 = wave * 4u;
   const uint16_t* rows[4];
   const float* csk[4];
   int64_t posk[4];
   uint32_t badk[4];
-  uint8_t* reck[4];  // the token's record or row, or nullptr: nothing to write
+  uint8_t* reck[4];  // the token's row, or nullptr: nothing to write
   int64_t slotk[4];
   // The slot and position loads are issued first and the row reads right
   // after, with nothing in between that waits for the former (the scheduling
@@ -975,75 +974,31 @@ __device__ __forceinline__ void kvi_body(const KviParams& p, uint32_t wave, uint
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (t0 + k >= p.n_tokens) slotk[k] = -1;
-    reck[k] = nullptr;
-    if (slotk[k] >= 0 && slotk[k] < p.num_slots) {  // else: padding token, or no such slot
-      if (OUT == kOutBf16) {
-        reck[k] = p.cache + slotk[k] * p.block_stride;
-      } else {
-        const uint32_t blk_i = magic_div((uint32_t)slotk[k], p.div_bs);
-        const uint32_t idx = (uint32_t)slotk[k] - blk_i * p.bs;
-        reck[k] = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
-      }
-    }
+    // else: padding token, or no such slot
+    reck[k] = slotk[k] >= 0 && slotk[k] < p.num_slots ? p.cache + slotk[k] * p.block_stride
+                                                       : nullptr;
   }
   transpose_rows(lds_wave, raw, lane, w);
 
-  if constexpr (OUT == kOutBf16) {
-    Vals v;
-    unpack_bf16(w, v);
-    if (L >= 12) rope_lane<false>(v, cs);
-    uint4 outv[4];
-    pack_bf16(v, outv);
-    if (PICK_ROW(q, badk) != 0) {  // position outside the table: a NaN row
+  Vals v;
+  unpack_bf16(w, v);
+  if (L >= 12) rope_lane<false>(v, cs);
+  uint4 outv[4];
+  pack_bf16(v, outv);
+  if (PICK_ROW(q, badk) != 0) {  // position outside the table: a NaN row
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    }
-    bool ok[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ok[k] = reck[k] != nullptr;
-    store_rows_bf16<kStoreNt>(lds_wave, outv, lane, reck, ok);
-  } else {
-    uint8_t* const rec = PICK_ROW(q, reck);
-    // Rows with nothing to write skip the rest; no early return, so a caller
-    // that inlines this body keeps a plain if/else around it.
-    if (rec) {
-      const int d0 = lane_dim0(L);
-
-      Vals v;
-      unpack_bf16(w, v);
-      if (L >= 12) rope_lane<false>(v, cs);
-      float scale;
-      uint32_t ebyte, codes[8];
-      quantize_lane<OUT>(v, p.eps, scale, ebyte, codes);
-      uint32_t word = 0;
-      if (OUT == RQ_SCALE_UE8M0) word = pack_ue8m0(ebyte, blk);
-      // nontemporal, as kvi2_kernel's for large launches (this body serves
-      // the fused kernel, whose kv records ride on a q launch of hundreds of
-      // MB): 261.8 -> 258.6 us for the fused 8192-token forward
-      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-      typedef __attribute__((address_space(1))) u32x2_t* gptr_u32x2;
-      typedef __attribute__((address_space(1))) uint32_t* gptr_u32;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        __builtin_nontemporal_store(u32x2_t{codes[2 * k], codes[2 * k + 1]},
-                                    (gptr_u32x2)(rec + d0 + 32 * k));
-      if (r == 0) {
-        // a token whose position is outside the table gets NaN scales
-        const bool bad = PICK_ROW(q, badk) != 0;
-        uint32_t tail;
-        if (OUT == RQ_SCALE_UE8M0) tail = (blk == 0) ? (bad ? 0xFFFFFFFFu : word) : 0u;
-        else tail = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, scale);
-        __builtin_nontemporal_store(tail, (gptr_u32)(rec + kHeadDim + 4 * blk));
-      }
-    }
+    for (int k = 0; k < 4; ++k)
+      outv[k] = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
   }
+  bool ok[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ok[k] = reck[k] != nullptr;
+  store_rows_bf16<kStoreNt>(lds_wave, outv, lane, reck, ok);
 }
 
-template <int OUT>
-__global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
+__global__ __launch_bounds__(256) void kvf_kernel(KviParams p) {
   extern __shared__ uint4 lds[];
-  kvi_body<OUT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
+  kvf_body(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
 }
 
 // kv_rope_quant_insert standalone, two tokens per wave: the lane layout of
@@ -1051,27 +1006,24 @@ __global__ __launch_bounds__(256) void kvi_kernel(KviParams p) {
 // 16b + r and 16b + 8 + r, quant block b on 8-lane group b), the forward
 // rotation, and each token's 528-byte record written as 33 16-byte granules:
 // the codes by lanes 32h .. 32h+31 through LDS, the scale tail by lane 32h.
-// With four tokens per wave (kvi_body, which the fused kernel and the bf16
-// cache use) these launches ran 2-7% slower; for the bf16 cache the
-// two-token form was slower from 8192 tokens on.  NT: the record stores are
+// With four tokens per wave these launches ran 2-7% slower.  The fused kernel
+// runs the same body for its kv waves.  NT: the record stores are
 // nontemporal.  Records land at the caller's slots, scattered over the
 // cache, and share their first and last 128-byte lines with records written
 // at other times or not at all; from 4096 tokens on, nontemporal stores
 // measured 7-20% faster, below that plain ones up to 4% faster (the host
 // picks by token count).
 template <int FMT, bool NT>
-__global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
-  extern __shared__ uint4 lds[];
+__device__ __forceinline__ void kvi2_body(const KviParams& p, uint32_t wave, uint4* lds_wave) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, L = lane & 31, b = L >> 3, r = L & 7;
-  const uint32_t t0 = wave_index(p.hdr) * 2u;
-  uint4* lds_wave = lds + 128 * (threadIdx.x >> 6);
+  const uint32_t t0 = wave * 2u;
   const uint16_t* rows[2];
   const float* csk[2];
   int64_t posk[2], slotk[2];
   uint32_t badk[2];
   uint8_t* reck[2];  // the token's record, or nullptr: nothing to write
-  // load order as in kvi_body: slots and positions, rows, then cos/sin
+  // load order as in kvf_body: slots and positions, rows, then cos/sin
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint32_t t = min(t0 + k, p.n_tokens - 1u);
@@ -1190,6 +1142,12 @@ __global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
   }
 }
 
+template <int FMT, bool NT>
+__global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
+  extern __shared__ uint4 lds[];
+  kvi2_body<FMT, NT>(p, wave_index(p.hdr), lds + 128 * (threadIdx.x >> 6));
+}
+
 // The q path and the kv path in one launch ([P1] section 1: the op
 // normalizes and rotates q and inserts the rotated kv in a single kernel;
 // section 2 names the full-cache forms: q as bf16 (in place) or FP8, kv into
@@ -1211,7 +1169,8 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
   uint4* lds_wave = lds + 256 * (threadIdx.x >> 6);
   const uint32_t w = wave_index(p.hdr);
   if (w >= p.q_waves) {
-    kvi_body<KOUT>(p.k, w - p.q_waves, lds_wave);
+    if constexpr (KOUT == kOutBf16) kvf_body(p.k, w - p.q_waves, lds_wave);
+    else kvi2_body<KOUT, true>(p.k, w - p.q_waves, lds_wave);
     // The compiler lays the two paths out one after the other; with the kv
     // stores drained here, the q path's loads keep their per-load waits.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1778,11 +1737,12 @@ const void* fused_fn(bool has_weight) {
                     : (const void*)fused_qnr_kvi_kernel<false, QOUT, KOUT>;
 }
 
-// One grid for both paths: q waves first, then kv waves.  `launch` sizes
-// grids in 16-lane rows, 4 per wave.
-int launch_fused(const void* fn, FusedParams& p, void* stream) {
+// One grid for both paths: q waves first, then kv waves of
+// `kv_tokens_per_wave` tokens (2 for the paged FP8 cache, 4 for the bf16
+// one).  `launch` sizes grids in 16-lane rows, 4 per wave.
+int launch_fused(const void* fn, FusedParams& p, void* stream, uint32_t kv_tokens_per_wave) {
   p.q_waves = (p.q.units + 3u) / 4u;
-  const uint32_t kv_waves = (p.k.n_tokens + 3u) / 4u;
+  const uint32_t kv_waves = (p.k.n_tokens + kv_tokens_per_wave - 1u) / kv_tokens_per_wave;
   return launch(fn, 4u * (p.q_waves + kv_waves), kFusedShape, &p, (hipStream_t)stream);
 }
 
@@ -1853,7 +1813,7 @@ int kv_rope_insert_full(const uint16_t* kv, int64_t kv_stride_token, const int64
   const int rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping,
                           n_tokens, cache, num_slots, cache_stride_token, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  return launch((const void*)kvi_kernel<kOutBf16>, p.n_tokens, kKviShape, &p,
+  return launch((const void*)kvf_kernel, p.n_tokens, kKviShape, &p,
                 (hipStream_t)stream);
 }
 
@@ -1878,7 +1838,7 @@ int qnorm_rope_kv_rope_quant_insert(
   const bool w = norm_weight != nullptr;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? fused_fn<kOutBf16, RQ_SCALE_UE8M0>(w)
                                                : fused_fn<kOutBf16, RQ_SCALE_FP32>(w);
-  return launch_fused(fn, p, stream);
+  return launch_fused(fn, p, stream, 2);
 }
 
 int qnorm_rope_kv_rope_insert_full(
@@ -1897,7 +1857,7 @@ int qnorm_rope_kv_rope_insert_full(
   rc = prep_kvf(kv, kv_stride_token, positions, cos_sin_cache, max_pos, slot_mapping, n_tokens,
                 cache, num_slots, cache_stride_token, p.k, ek);
   if (rc != RQ_OK || eq) return rc;
-  return launch_fused(fused_fn<kOutBf16, kOutBf16>(norm_weight != nullptr), p, stream);
+  return launch_fused(fused_fn<kOutBf16, kOutBf16>(norm_weight != nullptr), p, stream, 4);
 }
 
 int qnorm_rope_fp8_kv_rope_insert_full(
@@ -1920,7 +1880,7 @@ int qnorm_rope_fp8_kv_rope_insert_full(
   const bool w = norm_weight != nullptr;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? fused_fn<RQ_SCALE_UE8M0, kOutBf16>(w)
                                                : fused_fn<RQ_SCALE_FP32, kOutBf16>(w);
-  return launch_fused(fn, p, stream);
+  return launch_fused(fn, p, stream, 4);
 }
 
 int indexer_q_rope_quant(const uint16_t* q, int64_t q_stride_token, int64_t q_stride_head,
