@@ -188,9 +188,11 @@ def stream_lib():
         L.bench_stream_read.argtypes = [P, U64, U32, P, P]
         L.bench_stream_write.argtypes = [P, U64, I, P]
         L.bench_stream_irq.argtypes = [P, P, P, U64, I, P]
+        L.bench_stream_rows_gm.argtypes = [P, P, U64, U32, U32, P]
+        L.bench_stream_q.argtypes = [P, P, P, U64, U32, U32, I, P]
         L.bench_stream_empty.argtypes = [P]
         for f in (L.bench_stream_read, L.bench_stream_write, L.bench_stream_irq,
-                  L.bench_stream_empty):
+                  L.bench_stream_rows_gm, L.bench_stream_q, L.bench_stream_empty):
             f.restype = I
         _stream_lib = L
     return _stream_lib
@@ -256,6 +258,43 @@ def bench_stream(args, device, stream):
                                      buffer_sets=sets)
             del fns
         del rot
+        torch.cuda.empty_cache()
+
+    # inv_rope_bf16's pattern at its workload (16384 x 32 units, 1 KiB read
+    # and 1 KiB written group-major per unit, 4 groups of 8 heads)
+    units, heads, hpg = 16384 * 32, 32, 8
+    b = units * 2048
+    sets = rotation_sets(b)
+    rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
+            torch.empty(units * 1024, dtype=torch.uint8, device=device)) for _ in range(sets)]
+    fns = [lambda s_=s_, d=d: _ok(L.bench_stream_rows_gm(s_.data_ptr(), d.data_ptr(), units, heads,
+                                                         hpg, h()), "rows_gm")
+           for s_, d in rot]
+    ms = time_rotating(fns, args.steps, args.warmup, stream)
+    res["irb_pattern"] = dict(_rate("inv_rope_bf16's bytes for 16384 x 32 units (1 KiB read, "
+                                    "1 KiB written group-major), 4 units per wave, no math",
+                                    ms * 1e3, b), buffer_sets=sets)
+    del fns, rot
+    torch.cuda.empty_cache()
+
+    # the q paths' pattern at their workload (8192 tokens, 64 live heads padded
+    # to 128): qnorm_rope's bf16 rows, and qnorm_rope_fp8's codes and scales
+    tokens, hq, hpad = 8192, 64, 128
+    units = tokens * hpad
+    for key, out_bytes, what in (("qnr_pattern", 1024, "qnorm_rope"),
+                                 ("qf8_pattern", 512, "qnorm_rope_fp8")):
+        b = tokens * hq * 1024 + units * (out_bytes + (16 if out_bytes == 512 else 0))
+        sets = rotation_sets(b)
+        rot = [(torch.empty(tokens * hq * 1024, dtype=torch.uint8, device=device).fill_(3),
+                torch.empty(units * out_bytes, dtype=torch.uint8, device=device),
+                torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
+        fns = [lambda s_=s_, d=d, sc=sc, ob=out_bytes: _ok(L.bench_stream_q(
+            s_.data_ptr(), d.data_ptr(), sc.data_ptr(), units, hq, hpad, ob, h()), "q")
+            for s_, d, sc in rot]
+        ms = time_rotating(fns, args.steps, args.warmup, stream)
+        res[key] = dict(_rate(f"{what}'s bytes for 8192 x 64 -> 128 heads, 4 units per wave, "
+                              "no math", ms * 1e3, b), buffer_sets=sets)
+        del fns, rot
         torch.cuda.empty_cache()
 
     # at the kv insert's size (8192 units, 12.7 MB), timed as that kernel is:
@@ -340,9 +379,18 @@ SAME_SIZE_STREAMS = (
 
 def vs_same_size_stream(extra, ceiling):
     """Beside each shorter launch, the streaming pattern's rate at its size
-    (four units per wave, as the kernels, and two)."""
+    (four units per wave, as the kernels, and two); beside inv_rope_bf16, the
+    stream of its own byte pattern, and so beside the q paths."""
     if not ceiling:
         return
+    for what, key in (("inv_rope_bf16", "irb_pattern"), ("qnorm_rope", "qnr_pattern"),
+                      ("qnorm_rope_fp8", "qf8_pattern")):
+        if what in extra and key in ceiling:
+            # time ratio: the pattern moves the op's bytes less its per-token
+            # positions and cos/sin rows
+            extra[what]["pattern_stream_us"] = round(ceiling[key]["us"], 2)
+            extra[what]["frac_of_pattern_stream"] = round(
+                ceiling[key]["us"] / extra[what]["us"], 4)
     for key, _, what in SAME_SIZE_STREAMS:
         if what in extra and key in ceiling:
             extra[what]["same_size_stream_gbs"] = round(ceiling[key]["gbs"], 1)

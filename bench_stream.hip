@@ -17,6 +17,18 @@
 //                       (without it the same bytes took 5% longer); four
 //                       units per wave (the library's common structure) or
 //                       two (inv_rope_fp8_quant's);
+//   * stream_rows_gm  - inv_rope_bf16's traffic per 512-dim unit: a 1 KiB row
+//                       read and a 1 KiB row written, group-major as that
+//                       op writes them ([G, tokens, hpg rows]), four units per
+//                       wave in 256-thread workgroups dealt to the XCDs in
+//                       chunks of 64, through LDS as above;
+//   * stream_q        - the q paths' traffic per unit of a head-padded output:
+//                       a 1 KiB row read for a live head (none for a pad
+//                       head), then 1 KiB written (qnorm_rope's bf16 rows) or
+//                       512 bytes and a 16-byte scale group (qnorm_rope_fp8),
+//                       the rows with sc1 buffer stores as those kernels,
+//                       four units per wave in 256-thread workgroups dealt to
+//                       the XCDs in chunks of 16, through LDS;
 //   * stream_empty    - a launch that does nothing: the fixed cost of one
 //                       launch on a stream.
 // Every kernel covers exactly `rows` rows; the host sizes the grid so that no
@@ -120,8 +132,10 @@ __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* c
 #pragma unroll
   for (int k = 0; k < U / 2; ++k) {
     const uint64_t u = u0 + 2 * k + half;
-    // something from every row read, so no load is dead
-    const u32x4_t w = in[2 * k + half] ^ in[2 * k + 1 - half];
+    // something from every row read, so no load is dead (the same for both
+    // halves: a per-lane pick of the register array would cost hundreds of
+    // selects)
+    const u32x4_t w = in[2 * k] ^ in[2 * k + 1];
     if (u < units) __builtin_nontemporal_store(w, (gptr)(codes + u * 512 + 16 * j));
   }
   // unit k's scales from lane 16 k
@@ -132,6 +146,104 @@ __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* c
     for (int k = 1; k < U; ++k)
       if (row == (uint32_t)k) s = in[k];
     *(gptr)(scales + (u0 + row) * 16) = s;
+  }
+}
+
+// Per unit u = (t, h) of `units` = tokens x 2^heads_log2: read the 1 KiB row
+// u of src, write it (through LDS, lanes permuted) as row j of group
+// g = h / 2^hpg_log2, token t of dst, group-major:
+// dst + ((g * tokens + t) * 2^hpg_log2 + j) KiB.  (Powers of two, so that the
+// index arithmetic is shifts: a division by a runtime value would cost more
+// than the rest of the kernel.)
+__global__ __launch_bounds__(256) void stream_rows_gm(const uint8_t* src, uint8_t* dst,
+                                                      uint64_t units, uint32_t heads_log2,
+                                                      uint32_t hpg_log2) {
+  extern __shared__ u32x4_t lds[];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t u0 = (uint64_t)wave_id(6) * 4;
+  const uint64_t tokens = units >> heads_log2;
+  u32x4_t in[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t u = u0 + k < units ? u0 + k : units - 1;
+    in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
+  }
+  u32x4_t* slice = lds + 256 * (threadIdx.x >> 6);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) slice[64 * k + lane] = in[k];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) in[k] = slice[64 * k + (lane ^ 5)];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t u = u0 + k;
+    if (u < units) {
+      const uint64_t t = u >> heads_log2, h = u & ((1u << heads_log2) - 1u);
+      const uint64_t row = (((h >> hpg_log2) * tokens + t) << hpg_log2) + (h & ((1u << hpg_log2) - 1u));
+      __builtin_nontemporal_store(in[k], (gptr)(dst + row * 1024 + 16 * lane));
+    }
+  }
+}
+
+// Per unit u = (t, h) of `units` = tokens x 2^hpad_log2: a live head (h < hq)
+// reads row t * hq + h of src; every unit writes out_bytes (1024, or 512 and
+// 16 scale bytes) at dst + u * out_bytes (and scales + 16 u).
+template <int OUT_BYTES>
+__global__ __launch_bounds__(256) void stream_q(const uint8_t* src, uint8_t* dst, uint8_t* scales,
+                                                uint64_t units, uint32_t hq, uint32_t hpad_log2) {
+  extern __shared__ u32x4_t lds[];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t u0 = (uint64_t)wave_id(4) * 4;
+  u32x4_t in[4] = {};
+  bool live[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t u = u0 + k < units ? u0 + k : units - 1;
+    const uint64_t t = u >> hpad_log2, h = u & ((1u << hpad_log2) - 1u);
+    live[k] = h < hq;
+    if (live[k]) in[k] = __builtin_nontemporal_load((gptr_c)(src + (t * hq + h) * 1024 + 16 * lane));
+  }
+  u32x4_t* slice = lds + 256 * (threadIdx.x >> 6);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) slice[64 * k + lane] = in[k];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) in[k] = slice[64 * k + (lane ^ 5)];
+  // the rows go out as the q kernels write them: buffer stores with the sc1
+  // cache-policy bit
+  if (OUT_BYTES == 1024) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (u0 + k < units) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(dst + (u0 + k) * 1024, 0, 1024, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(in[k], rs, 16 * lane, 0, 16);
+      }
+  } else {
+    const uint32_t half = lane >> 5, j = lane & 31;
+    // one resource over the wave's four 512-byte rows (a tail wave's missing
+    // rows are never written: the guard below)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(dst + u0 * 512, 0, 4 * 512, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint64_t u = u0 + 2 * k + half;
+      const u32x4_t w = in[2 * k] ^ in[2 * k + 1];  // as in stream_irq
+      if (u < units) __builtin_amdgcn_raw_buffer_store_b128(w, rs, 512 * (2 * k + half) + 16 * j, 0, 16);
+    }
+    // unit k's scale group from lane 16 k
+    const uint32_t row = lane >> 4;
+    if ((lane & 15) == 0 && u0 + row < units) {
+      u32x4_t sv = in[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k)
+        if (row == (uint32_t)k) sv = in[k];
+      *(gptr)(scales + (u0 + row) * 16) = sv;
+    }
   }
 }
 
@@ -174,6 +286,37 @@ int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units,
   else if (units_per_wave == 2)
     hipLaunchKernelGGL(stream_irq<2>, dim3(grid_for(units, 4)), dim3(128), 2 * 2048, s,
                        (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int bench_stream_rows_gm(const void* src, void* dst, uint64_t units, uint32_t heads,
+                         uint32_t hpg, void* stream) {
+  // heads and hpg powers of two, hpg <= heads
+  if (units == 0 || units > (1ull << 36) || heads == 0 || hpg == 0 || (heads & (heads - 1)) ||
+      (hpg & (hpg - 1)) || heads % hpg || units % heads)
+    return -1;
+  hipLaunchKernelGGL(stream_rows_gm, dim3(grid_for(units, 16)), dim3(256), 4 * 4096,
+                     (hipStream_t)stream, (const uint8_t*)src, (uint8_t*)dst, units,
+                     (uint32_t)__builtin_ctz(heads), (uint32_t)__builtin_ctz(hpg));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int bench_stream_q(const void* src, void* dst, void* scales, uint64_t units, uint32_t hq,
+                   uint32_t hpad, int out_bytes, void* stream) {
+  // hpad a power of two
+  if (units == 0 || units > (1ull << 36) || hq == 0 || hpad < hq || (hpad & (hpad - 1)) ||
+      units % hpad)
+    return -1;
+  const hipStream_t s = (hipStream_t)stream;
+  const uint32_t hl = (uint32_t)__builtin_ctz(hpad);
+  if (out_bytes == 1024)
+    hipLaunchKernelGGL(stream_q<1024>, dim3(grid_for(units, 16)), dim3(256), 4 * 4096, s,
+                       (const uint8_t*)src, (uint8_t*)dst, (uint8_t*)scales, units, hq, hl);
+  else if (out_bytes == 512 && scales)
+    hipLaunchKernelGGL(stream_q<512>, dim3(grid_for(units, 16)), dim3(256), 4 * 4096, s,
+                       (const uint8_t*)src, (uint8_t*)dst, (uint8_t*)scales, units, hq, hl);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
