@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 STREAM_SRC = os.path.join(ROOT, "bench_stream.hip")
 STREAM_LIB = os.path.join(ROOT, "bench_stream.so")
+STREAM_DIRECT = 0x100  # bench_stream_irq: rows read with LDS-direct loads
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "irq_prefill_n16384_h32_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", "ropequant.hip")
 
@@ -249,13 +250,15 @@ def bench_stream(args, device, stream):
         rot = [(torch.empty(units * 1024, dtype=torch.uint8, device=device).fill_(3),
                 torch.empty(units * 512, dtype=torch.uint8, device=device),
                 torch.empty(units * 16, dtype=torch.uint8, device=device)) for _ in range(sets)]
-        for upw, suffix in ((4, ""), (2, "_2_per_wave")):
+        for upw, suffix in ((4, ""), (2, "_2_per_wave"), (4 | STREAM_DIRECT, "_direct"),
+                            (2 | STREAM_DIRECT, "_2_per_wave_direct")):
             fns = [lambda s_=s_, c=c, sc=sc, u=units, upw=upw: _ok(L.bench_stream_irq(
                 s_.data_ptr(), c.data_ptr(), sc.data_ptr(), u, upw, h()), "irq")
                 for s_, c, sc in rot]
             ms = time_rotating(fns, args.steps, args.warmup, stream)
-            res[key + suffix] = dict(_rate(f"{what}, {upw} units per wave, no math", ms * 1e3, b),
-                                     buffer_sets=sets)
+            how = " read straight into LDS" if upw & STREAM_DIRECT else ""
+            res[key + suffix] = dict(_rate(f"{what}, {upw & 0xFF} units per wave{how}, no math",
+                                           ms * 1e3, b), buffer_sets=sets)
             del fns
         del rot
         torch.cuda.empty_cache()

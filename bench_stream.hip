@@ -16,7 +16,8 @@
 //                       between the reads and the writes as the kernels make
 //                       (without it the same bytes took 5% longer); four
 //                       units per wave (the library's common structure) or
-//                       two (inv_rope_fp8_quant's);
+//                       two (inv_rope_fp8_quant's); each also with the rows
+//                       read straight into LDS (global_load_lds_dwordx4);
 //   * stream_rows_gm  - inv_rope_bf16's traffic per 512-dim unit: a 1 KiB row
 //                       read and a 1 KiB row written, group-major as that
 //                       op writes them ([G, tokens, hpg rows]), four units per
@@ -106,26 +107,45 @@ __global__ __launch_bounds__(256) void stream_write(uint8_t* dst, uint64_t rows,
 // does with group-major outputs.  U units per wave (4, as the kernel, or 2);
 // each store instruction writes two units' code rows, lanes 0..31 the even
 // unit and lanes 32..63 the odd one, 16 bytes each.
-template <int U>
+//
+// DIRECT: the rows go straight into the wave's LDS slice instead
+// (global_load_lds_dwordx4, nontemporal: lane i's 16 bytes land at byte 16 i
+// of the destination), with no VGPR staging and no LDS write instruction;
+// the wait for those LDS writes is explicit, since the compiler does not
+// order LDS reads after these loads by itself.
+constexpr short kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0); expcnt, lgkmcnt left alone
+
+template <int U, bool DIRECT>
 __global__ __launch_bounds__(128) void stream_irq(const uint8_t* src, uint8_t* codes,
                                                   uint8_t* scales, uint64_t units) {
   extern __shared__ u32x4_t lds[];
   const uint32_t lane = threadIdx.x & 63;
   const uint64_t u0 = (uint64_t)wave_id(6) * U;
-  u32x4_t in[U];
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const uint64_t u = u0 + k < units ? u0 + k : units - 1;
-    in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
-  }
-  // through the wave's U KiB of LDS and back, lanes permuted, as the kernel's
-  // transpose does
   u32x4_t* slice = lds + 64 * U * (threadIdx.x >> 6);
+  u32x4_t in[U];
+  if (DIRECT) {
 #pragma unroll
-  for (int k = 0; k < U; ++k) slice[64 * k + lane] = in[k];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int k = 0; k < U; ++k) {
+      const uint64_t u = u0 + k < units ? u0 + k : units - 1;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + u * 1024 + 16 * lane),
+          (__attribute__((address_space(3))) void*)(slice + 64 * k), 16, 0, 2 /* nt */);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint64_t u = u0 + k < units ? u0 + k : units - 1;
+      in[k] = __builtin_nontemporal_load((gptr_c)(src + u * 1024 + 16 * lane));
+    }
+    // through the wave's U KiB of LDS and back, lanes permuted, as the
+    // kernel's transpose does
+#pragma unroll
+    for (int k = 0; k < U; ++k) slice[64 * k + lane] = in[k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 #pragma unroll
   for (int k = 0; k < U; ++k) in[k] = slice[64 * k + (lane ^ 5)];
   const uint32_t half = lane >> 5, j = lane & 31;
@@ -276,16 +296,27 @@ int bench_stream_write(void* dst, uint64_t rows, int policy, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// units_per_wave: 4 or 2, or either | kDirect for the direct-to-LDS reads
+constexpr int kDirect = 0x100;
+
 int bench_stream_irq(const void* src, void* codes, void* scales, uint64_t units,
                      int units_per_wave, void* stream) {
   if (units == 0 || units > (1ull << 36)) return -1;
   const hipStream_t s = (hipStream_t)stream;
+  const uint8_t* in = (const uint8_t*)src;
+  uint8_t *c = (uint8_t*)codes, *sc = (uint8_t*)scales;
   if (units_per_wave == 4)
-    hipLaunchKernelGGL(stream_irq<4>, dim3(grid_for(units, 8)), dim3(128), 2 * 4096, s,
-                       (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+    hipLaunchKernelGGL((stream_irq<4, false>), dim3(grid_for(units, 8)), dim3(128), 2 * 4096, s,
+                       in, c, sc, units);
   else if (units_per_wave == 2)
-    hipLaunchKernelGGL(stream_irq<2>, dim3(grid_for(units, 4)), dim3(128), 2 * 2048, s,
-                       (const uint8_t*)src, (uint8_t*)codes, (uint8_t*)scales, units);
+    hipLaunchKernelGGL((stream_irq<2, false>), dim3(grid_for(units, 4)), dim3(128), 2 * 2048, s,
+                       in, c, sc, units);
+  else if (units_per_wave == (4 | kDirect))
+    hipLaunchKernelGGL((stream_irq<4, true>), dim3(grid_for(units, 8)), dim3(128), 2 * 4096, s,
+                       in, c, sc, units);
+  else if (units_per_wave == (2 | kDirect))
+    hipLaunchKernelGGL((stream_irq<2, true>), dim3(grid_for(units, 4)), dim3(128), 2 * 2048, s,
+                       in, c, sc, units);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
