@@ -19,8 +19,9 @@ SCALE_FP32 = 0
 SCALE_UE8M0 = 1
 RECORD_BYTES = 528
 # RMSNorm summation orders: "index" is the definition (left to right over the
-# 512 dims); "tree" adds the same squares in a fixed 64-chunk tree.
-SUM_ORDERS = {"index": 0, "tree": 1}
+# 512 dims); "pairwise" adds the same squares by recursive pairwise summation
+# (each half-range's sum added to the other's).
+SUM_ORDERS = {"index": 0, "pairwise": 1}
 
 
 def _order(sum_order):
@@ -63,7 +64,9 @@ def lib():
         L.orc_rope_head.restype = None
         L.orc_quant_head.argtypes = [P, ctypes.c_int, ctypes.c_float, P, P, P]
         L.orc_quant_head.restype = None
-        for nm in ("orc_rmsnorm_head", "orc_rmsnorm_head_tree"):
+        L.orc_sum_squares.argtypes = [P, I32, I32]
+        L.orc_sum_squares.restype = ctypes.c_float
+        for nm in ("orc_rmsnorm_head", "orc_rmsnorm_head_pairwise"):
             getattr(L, nm).argtypes = [P, P, ctypes.c_float, P]
             getattr(L, nm).restype = None
         L.orc_inv_rope_fp8_quant.argtypes = [P, I64, I64, P, P, I64, I64, I32, I32, I32, D,
@@ -182,12 +185,21 @@ def quant_head(x, scale_fmt=SCALE_FP32, eps=1e-10):
     return codes, sc, int(word[0])
 
 
+def sum_squares(x, sum_order="index"):
+    """RMSNorm's fp32 sum of squares of x (1-D, at least one value), the
+    squares added in `sum_order`."""
+    x = _need(np.ascontiguousarray(x, dtype=np.float32), np.float32, "x")
+    if x.ndim != 1 or x.size < 1:
+        raise ValueError("x must be a non-empty vector")
+    return np.float32(lib().orc_sum_squares(_ptr(x), x.size, _order(sum_order)))
+
+
 def rmsnorm_head(x, weight_bits, eps, sum_order="index"):
     """RMSNorm of one 512-dim fp32 head; the squares are added in `sum_order`."""
     x = _need(np.ascontiguousarray(x, dtype=np.float32), np.float32, "x")
     w = None if weight_bits is None else np.ascontiguousarray(weight_bits, dtype=np.uint16)
     y = np.empty(512, dtype=np.float32)
-    fn = lib().orc_rmsnorm_head_tree if _order(sum_order) else lib().orc_rmsnorm_head
+    fn = lib().orc_rmsnorm_head_pairwise if _order(sum_order) else lib().orc_rmsnorm_head
     fn(_ptr(x), _ptr(w), float(np.float32(eps)), _ptr(y))
     return y
 
@@ -265,7 +277,7 @@ def inv_rope_bf16(o_bits, positions, cos_sin_cache, heads_per_group, layout="gro
 def qnorm_rope(q_bits, weight_bits, positions, cos_sin_cache, q_head_padded, eps,
                sum_order="index"):
     """Oracle QNR: q_bits uint16 [N, Hq, 512] -> q_out uint16 [N, Hpad, 512].
-    sum_order: "index" (the RMSNorm definition) or "tree" (see SUM_ORDERS)."""
+    sum_order: "index" (the RMSNorm definition) or "pairwise" (see SUM_ORDERS)."""
     q_bits = _need(q_bits, np.uint16, "q_in")
     positions = _need(positions, np.int64, "positions")
     cos_sin_cache = _need(cos_sin_cache, np.float32, "cos_sin_cache")

@@ -226,7 +226,7 @@ void orc_quant_head(const float* x, int scale_fmt, float eps, uint8_t* codes,
  *   r = 1 / sqrt(mean + eps)  (correctly rounded sqrt, then divide);
  *   y_d = (x_d * r) * w_d, or x_d * r when there is no weight.
  * The pages fix no summation order; index order is the plain reading of
- * "mean(x^2)".  orc_rmsnorm_head_tree below differs only in that order. */
+ * "mean(x^2)".  orc_rmsnorm_head_pairwise below differs only in that order. */
 static void rms_apply(const float* x, const uint16_t* weight, float eps, float ss, float* y) {
   int d;
   float mean = ss / 512.0f;
@@ -237,40 +237,50 @@ static void rms_apply(const float* x, const uint16_t* weight, float eps, float s
   }
 }
 
-void orc_rmsnorm_head(const float* x, const uint16_t* weight, float eps, float* y) {
+/* x_0^2 + x_1^2 + ... + x_{n-1}^2, added left to right */
+static float sum_squares_index(const float* x, int n) {
   int d;
   float ss = x[0] * x[0];
-  for (d = 1; d < HEAD_DIM; ++d) ss = ss + x[d] * x[d];
-  rms_apply(x, weight, eps, ss, y);
+  for (d = 1; d < n; ++d) ss = ss + x[d] * x[d];
+  return ss;
 }
 
-/* The same RMSNorm with the squares added in another fixed order, a tree:
- *   p_c = ((x_{8c}^2 + x_{8c+1}^2) + ...) + x_{8c+7}^2   for c = 0..63
- *   for k = 1, 2, 4, 8, 16, 32:  p_c <- p_c + p_{c xor k}  (all c at once)
- *   ss = p_0.
- * Not the definition: a second rounding order of the same sum, for tests
- * that separate the summation order from every other step. */
-void orc_rmsnorm_head_tree(const float* x, const uint16_t* weight, float eps, float* y) {
-  float p[64], t[64];
-  int c, d, k;
-  for (c = 0; c < 64; ++c) {
-    float acc = x[8 * c] * x[8 * c];
-    for (d = 1; d < 8; ++d) acc = acc + x[8 * c + d] * x[8 * c + d];
-    p[c] = acc;
-  }
-  for (k = 1; k < 64; k <<= 1) {
-    for (c = 0; c < 64; ++c) t[c] = p[c] + p[c ^ k];
-    for (c = 0; c < 64; ++c) p[c] = t[c];
-  }
-  rms_apply(x, weight, eps, p[0], y);
+void orc_rmsnorm_head(const float* x, const uint16_t* weight, float eps, float* y) {
+  rms_apply(x, weight, eps, sum_squares_index(x, HEAD_DIM), y);
+}
+
+/* Sum of x_i^2 over [0, n) by pairwise summation: the sums of the two
+ * halves [0, n/2) and [n/2, n), each found the same way, added; one term is
+ * its square.  Every square and every sum is one fp32 rounding.  (The
+ * recursive pairwise order analysed in N. J. Higham, "The accuracy of
+ * floating point summation", SIAM J. Sci. Comput. 14(4), 1993.) */
+static float sum_squares_pairwise(const float* x, int n) {
+  if (n == 1) return x[0] * x[0];
+  return sum_squares_pairwise(x, n / 2) + sum_squares_pairwise(x + n / 2, n - n / 2);
+}
+
+/* The same RMSNorm with the squares added by pairwise summation over the 512
+ * dims.  Not the definition's order: a second standard rounding order of the
+ * same sum, for tests that separate the summation order from every other
+ * step. */
+void orc_rmsnorm_head_pairwise(const float* x, const uint16_t* weight, float eps, float* y) {
+  rms_apply(x, weight, eps, sum_squares_pairwise(x, HEAD_DIM), y);
 }
 
 /* sum_order argument of the q-path ops: ORC_SUM_INDEX is the definition */
-enum { ORC_SUM_INDEX = 0, ORC_SUM_TREE = 1 };
+enum { ORC_SUM_INDEX = 0, ORC_SUM_PAIRWISE = 1 };
+
+/* The sum of squares RMSNorm uses, over n >= 1 values, in sum_order
+ * (exported so that tests can pin each order's sums themselves: a change of
+ * a few units in a sum near 2^24 can vanish in the rounded 1 / sqrt). */
+float orc_sum_squares(const float* x, int32_t n, int32_t sum_order) {
+  if (n < 1) return 0.0f;
+  return sum_order == ORC_SUM_PAIRWISE ? sum_squares_pairwise(x, n) : sum_squares_index(x, n);
+}
 
 static void rmsnorm_by_order(const float* x, const uint16_t* weight, float eps, int32_t order,
                              float* y) {
-  if (order == ORC_SUM_TREE) orc_rmsnorm_head_tree(x, weight, eps, y);
+  if (order == ORC_SUM_PAIRWISE) orc_rmsnorm_head_pairwise(x, weight, eps, y);
   else orc_rmsnorm_head(x, weight, eps, y);
 }
 
@@ -384,7 +394,7 @@ int orc_inv_rope_bf16(const uint16_t* o, int64_t o_stride_token, int64_t o_strid
  * [P1] section 1 (q_out preallocated, every element written, pad zeroed,
  * q_head_padded >= num_heads_q); [P3] section 5 (RMSNorm).
  * Reading: fp32 throughout, one bf16 rounding at the end.
- * sum_order: ORC_SUM_INDEX (the RMSNorm definition) or ORC_SUM_TREE. */
+ * sum_order: ORC_SUM_INDEX (the RMSNorm definition) or ORC_SUM_PAIRWISE. */
 int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_head,
                    const uint16_t* norm_weight, const int64_t* positions,
                    const float* cos_sin_cache, int64_t max_pos, int64_t n_tokens,
@@ -398,7 +408,7 @@ int orc_qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_strid
   if (n_tokens < 0 || n_heads_q <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
   if (q_head_padded < n_heads_q) return ORC_ERR_SHAPE;
   if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
-  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_PAIRWISE) return ORC_ERR_VALUE;
   if (n_tokens == 0) return ORC_OK;
   if (!q_in || !positions || !cos_sin_cache || !q_out) return ORC_ERR_NULL;
   for (t = 0; t < n_tokens; ++t)
@@ -435,7 +445,7 @@ int orc_qnorm_rope_f32(const uint16_t* q_in, int64_t q_stride_token, int64_t q_s
   float epsf = (float)eps;
   if (n_tokens < 0 || n_heads_q <= 0 || max_pos <= 0) return ORC_ERR_SHAPE;
   if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
-  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_PAIRWISE) return ORC_ERR_VALUE;
   if (n_tokens == 0) return ORC_OK;
   if (!q_in || !positions || !cos_sin_cache || !z_out) return ORC_ERR_NULL;
   for (t = 0; t < n_tokens; ++t)
@@ -478,7 +488,7 @@ int orc_qnorm_rope_fp8(const uint16_t* q_in, int64_t q_stride_token, int64_t q_s
   if (!(eps > 0.0) || !isfinite(eps) || !(epsf > 0.0f)) return ORC_ERR_VALUE;
   if (scale_fmt != ORC_SCALE_FP32 && scale_fmt != ORC_SCALE_UE8M0) return ORC_ERR_VALUE;
   if (!eps_ok(quant_eps)) return ORC_ERR_VALUE;
-  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_TREE) return ORC_ERR_VALUE;
+  if (sum_order != ORC_SUM_INDEX && sum_order != ORC_SUM_PAIRWISE) return ORC_ERR_VALUE;
   if (n_tokens == 0) return ORC_OK;
   if (!q_in || !positions || !cos_sin_cache || !q_fp8 || !q_scales) return ORC_ERR_NULL;
   for (t = 0; t < n_tokens; ++t)

@@ -733,18 +733,22 @@ struct QnrParams {
 };
 
 // RMSNorm of the lane's row ([P3] section 5), v <- (v * r) * w, in two
-// steps.  rms_inv: r = 1 / sqrt(mean(v^2) + eps), the sum of squares in a
-// fixed tree: chunk sums left to right, then butterflies over the chunk index
-// c = 16b + 4k + r for bit 0, 1 (lanes r^1, r^2), bit 2, 3 (this lane's k^1,
-// k^2), bit 4, 5 (quads b^1, b^2).
+// steps.  rms_inv: r = 1 / sqrt(mean(v^2) + eps), the sum of squares by
+// pairwise summation over the 512 dims (recursive halving: each half-range's
+// sum added to the other's, down to single squares).  Every level of that
+// tree is a pairing the lane layout already holds: dims 8c .. 8c+7 of chunk
+// c = 16b + 4k + r sit in one lane (levels 1-3, in registers); chunks c and
+// c^1, c^2 are lanes r^1, r^2 of the quad (levels 4-5, DPP); c^4, c^8 are
+// this lane's k^1, k^2 (levels 6-7); c^16, c^32 the quads b^1, b^2 (levels
+// 8-9, DPP).  Each lane ends with the same bits, as fp32 addition commutes.
 __device__ __forceinline__ float rms_inv(const Vals& v, float eps) {
   float ps[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float acc = v.x[k][0] * v.x[k][0];
+    float sq[8];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) acc = acc + v.x[k][e] * v.x[k][e];
-    ps[k] = acc;
+    for (int e = 0; e < 8; ++e) sq[e] = v.x[k][e] * v.x[k][e];
+    ps[k] = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) ps[k] = ps[k] + dpp_f32<kQuadSwap1>(ps[k]);

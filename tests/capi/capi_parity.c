@@ -8,7 +8,7 @@
  * except at most 1e-4 of them one adjacent code apart; qnorm_rope's bf16 rows
  * within one bf16 ulp of the oracle's RMSNorm definition (its squares summed
  * in index order) on at most 1e-3 of the elements, and bit for bit equal to
- * the oracle summing them in the kernel's tree order.  Also
+ * the oracle summing them by recursive pairwise summation.  Also
  * checks that a rejected call reports its status and launches nothing.
  *
  * Inputs come from a seeded xorshift generator in this file.  Prints one line
@@ -223,7 +223,7 @@ static void case_qnr(hipStream_t stream) {
     ++failures;
     return;
   }
-  check_bytes("qnorm_rope bf16 rows vs tree-order RMSNorm", (uint8_t*)out, (uint8_t*)eout,
+  check_bytes("qnorm_rope bf16 rows vs pairwise-summed RMSNorm", (uint8_t*)out, (uint8_t*)eout,
               n_out * 2);
   HIP_OK(hipFree(d_q));
   HIP_OK(hipFree(d_w));

@@ -10,8 +10,8 @@ Parity bar (GPU result vs the CPU oracle on identical inputs):
     fix: against the oracle's definition (index order), within bounds derived
     from the two orders' rounding (Q_RTOL below), with at most 1e-3 of the
     bf16 elements and 1e-4 of the codes differing; and bit for bit against
-    the oracle summing in the kernel's tree order, which isolates the
-    summation order from every other step.
+    the oracle summing by recursive pairwise summation, the kernel's order,
+    which isolates the summation order from every other step.
 """
 import numpy as np
 import torch
@@ -189,15 +189,15 @@ def assert_bf16_near_definition(got, z_def, exp, what):
 def assert_q_out_parity(got, q, w, pos, cache, hpad, eps, what):
     """QNR bf16 rows: pad heads exact, live heads within the derived slack of
     the RMSNorm definition, and bit for bit the oracle with the kernel's
-    summation order."""
+    summation order (pairwise)."""
     got = np.asarray(got, np.uint16)
     exp = oracle.qnorm_rope(q, w, pos, cache, hpad, eps)
     hq = q.shape[1]
     assert_bits_equal(got[:, hq:], exp[:, hq:], f"{what} pad heads")
     z = oracle.qnorm_rope_f32(q, w, pos, cache, eps)
     assert_bf16_near_definition(got[:, :hq], z, exp[:, :hq], f"{what} vs index-order RMSNorm")
-    exp_tree = oracle.qnorm_rope(q, w, pos, cache, hpad, eps, sum_order="tree")
-    assert_bits_equal(got, exp_tree, f"{what} vs tree-order RMSNorm")
+    exp_pw = oracle.qnorm_rope(q, w, pos, cache, hpad, eps, sum_order="pairwise")
+    assert_bits_equal(got, exp_pw, f"{what} vs pairwise-summed RMSNorm")
 
 
 def _scales_f32(sc, fmt):
@@ -247,7 +247,7 @@ def assert_fp8_near_definition(codes, sc, z_def, ec, es, fmt, what):
 def assert_q_fp8_parity(codes, sc, q, w, pos, cache, hpad, eps, fmt, what, quant_eps=1e-10):
     """FP8 q path: pad heads exact, live heads within the derived slack of the
     definition, and bit for bit (codes to the code bar) the oracle with the
-    kernel's summation order."""
+    kernel's summation order (pairwise)."""
     f = oracle.SCALE_UE8M0 if fmt == "ue8m0" else oracle.SCALE_FP32
     codes = np.asarray(codes, np.uint8)
     sc = np.asarray(sc)
@@ -258,6 +258,7 @@ def assert_q_fp8_parity(codes, sc, q, w, pos, cache, hpad, eps, fmt, what, quant
     z = oracle.qnorm_rope_f32(q, w, pos, cache, eps)
     assert_fp8_near_definition(codes[:, :hq], sc[:, :hq], z, ec[:, :hq], es[:, :hq], fmt,
                                f"{what} vs index-order RMSNorm")
-    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, hpad, eps, f, quant_eps, sum_order="tree")
-    assert_bits_equal(sc, es, f"{what} scales vs tree-order RMSNorm")
-    assert_codes_match(codes, ec, f"{what} codes vs tree-order RMSNorm")
+    ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, hpad, eps, f, quant_eps,
+                                   sum_order="pairwise")
+    assert_bits_equal(sc, es, f"{what} scales vs pairwise-summed RMSNorm")
+    assert_codes_match(codes, ec, f"{what} codes vs pairwise-summed RMSNorm")

@@ -18,5 +18,5 @@ def test_c_program_matches_the_oracle():
     print(res.stdout, res.stderr, flush=True)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.strip().endswith("capi parity OK")
-    # 2 per IRQ format, 2 QNR (index and tree RMSNorm order), 2 KVI, 1 rejected call
+    # 2 per IRQ format, 2 QNR (index and pairwise RMSNorm order), 2 KVI, 1 rejected call
     assert res.stdout.count("[capi]") == 9

@@ -53,11 +53,16 @@ MUTANTS = [
     ("RMSNorm weight reversed", "v * orc_bf16_to_f32(weight[d])",
      "v * orc_bf16_to_f32(weight[HEAD_DIM - 1 - d])"),
     ("RMSNorm squares summed right to left",
-     "  float ss = x[0] * x[0];\n  for (d = 1; d < HEAD_DIM; ++d) ss = ss + x[d] * x[d];",
-     "  float ss = x[HEAD_DIM - 1] * x[HEAD_DIM - 1];\n"
-     "  for (d = HEAD_DIM - 2; d >= 0; --d) ss = ss + x[d] * x[d];"),
-    ("tree order: butterflies reversed",
-     "for (k = 1; k < 64; k <<= 1) {", "for (k = 32; k > 0; k >>= 1) {"),
+     "  float ss = x[0] * x[0];\n  for (d = 1; d < n; ++d) ss = ss + x[d] * x[d];",
+     "  float ss = x[n - 1] * x[n - 1];\n"
+     "  for (d = n - 2; d >= 0; --d) ss = ss + x[d] * x[d];"),
+    ("pairwise sum split at a quarter",
+     "return sum_squares_pairwise(x, n / 2) + sum_squares_pairwise(x + n / 2, n - n / 2);",
+     "return sum_squares_pairwise(x, (n + 2) / 4) + sum_squares_pairwise(x + (n + 2) / 4, "
+     "n - (n + 2) / 4);"),
+    ("pairwise sum taken left to right",
+     "return sum_squares_pairwise(x, n / 2) + sum_squares_pairwise(x + n / 2, n - n / 2);",
+     "return sum_squares_pairwise(x, n - 1) + x[n - 1] * x[n - 1];"),
     ("IRQ scale index transposed", "(j * NBLOCK + b) * sc_stride_block",
      "(b * heads_per_group + j) * sc_stride_block"),
     ("IRQ codes at the token-major column", "out[g * out_stride_group + t * out_stride_token + "

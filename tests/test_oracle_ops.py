@@ -148,7 +148,7 @@ def test_qnr_end_to_end_fp64_within_one_bf16_ulp():
             assert (np.abs(got - y) <= ulp).all()
 
 
-@pytest.mark.parametrize("sum_order", ["index", "tree"])
+@pytest.mark.parametrize("sum_order", ["index", "pairwise"])
 def test_qnr_f32_is_what_the_q_paths_round(sum_order):
     # its bf16 rounding by torch's cast is qnorm_rope's live heads, its block
     # quantization is qnorm_rope_fp8's, and it agrees with an fp64 evaluation

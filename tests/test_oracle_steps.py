@@ -224,7 +224,7 @@ def _rms64(x, w, eps):
     return x * r * (1.0 if w is None else bf16_value(w).astype(np.float64))
 
 
-@pytest.mark.parametrize("sum_order", ["index", "tree"])
+@pytest.mark.parametrize("sum_order", ["index", "pairwise"])
 @pytest.mark.parametrize("eps", [1e-6, 0.5])
 def test_rmsnorm_matches_fp64(eps, sum_order):
     w = synth.uniform_bf16((512,), 3, synth.T_W, 0.5, 1.5)
@@ -261,41 +261,82 @@ def test_rmsnorm_index_order_hand_derived():
     # x = [2^12, 1 x 511].  Left to right, 2^24 + 1 lies halfway between 2^24
     # and 2^24 + 2 and rounds to the even 2^24, so each of the 511 additions
     # leaves 2^24: ss = 2^24.  The exact sum is 2^24 + 511; summed right to
-    # left it is 2^24 + 512 (511 + 2^24 ties to the even 2^24 + 512); the
-    # 64-chunk tree gives 2^24 + 504 (chunk 0 stays 2^24, the other 63 chunks
-    # are exact 8s that the butterflies add exactly).
+    # left it is 2^24 + 512 (511 + 2^24 ties to the even 2^24 + 512).
     x = np.ones(512, np.float32)
     x[0] = 2.0 ** 12
+    assert f32_bits(oracle.sum_squares(x)) == f32_bits(np.float32(2.0 ** 24))
     y = oracle.rmsnorm_head(x, None, 1e-6)
     r = _r_of_ss(2.0 ** 24)
     assert f32_bits(y[1]) == f32_bits(r)
     assert f32_bits(y[0]) == f32_bits(np.float32(2.0 ** 12) * r)
-    for other in (2.0 ** 24 + 511, 2.0 ** 24 + 512, 2.0 ** 24 + 504):
+    for other in (2.0 ** 24 + 511, 2.0 ** 24 + 512):
         assert _r_of_ss(other) != r  # the case tells the orders apart
-    yt = oracle.rmsnorm_head(x, None, 1e-6, sum_order="tree")
-    assert f32_bits(yt[1]) == f32_bits(_r_of_ss(2.0 ** 24 + 504))
 
 
-def test_rmsnorm_tree_order_hand_derived():
-    # Chunk 0 = [2^12, 1 x 7]: left to right, 2^24 + 1 rounds back to 2^24
-    # (tie to even) seven times -> 2^24.  Chunks 2 and 3 each hold [1, 0 x 7].
-    # Butterfly k=1 gives chunk0+chunk1 = 2^24 and chunk2+chunk3 = 2; k=2 adds
-    # them: 2^24 + 2 exactly.  (Left-to-right over all 512 dims gives 2^24;
-    # summing chunk 0 right-to-left would give 2^24 + 8.)
-    x = np.zeros(512, np.float32)
-    x[0] = 2.0 ** 12
-    x[1:8] = 1.0
-    x[16] = 1.0
-    x[24] = 1.0
+# Pairwise summation by hand.  A range's sum is its two halves' sums added
+# ([0, n/2) and [n/2, n)); a lone square is itself.  Near 2^24 fp32 holds the
+# even integers, and an odd one rounds to the even neighbour whose last
+# significand bit is 0: 2^24 + 1 -> 2^24, 2^24 + 3 -> 2^24 + 4.
+PAIRWISE_CASES = [
+    # x = [2^12, 1 x 511]: [0, 2) = 2^24 + 1 -> 2^24; every other range of 2^l
+    # dims is 2^l exactly; [0, 2^l) = 2^24 + 2 + 4 + ... + 2^(l-1) =
+    # 2^24 + 2^l - 2, exact, so [0, 512) = 2^24 + 510.  (Index order 2^24;
+    # exact 2^24 + 511; right to left 2^24 + 512; left to right within 8-dim
+    # chunks, then pairwise over the chunks, 2^24 + 504.)
+    ("ones", [2.0 ** 12] + [1.0] * 511, 2.0 ** 24 + 510),
+    # x = [2^12, 0, 1, 1, 0 x 508]: [0, 2) = 2^24, [2, 4) = 2, [0, 4) =
+    # 2^24 + 2, the rest zeros.  Adding a lone 1 to 2^24 first (index order,
+    # left to right within chunks, halving strides that pair dim i with
+    # i + n/2) gives 2^24.
+    ("pair", [2.0 ** 12, 0.0, 1.0, 1.0] + [0.0] * 508, 2.0 ** 24 + 2),
+    # ragged lengths: n = 3 is x0^2 + (x1^2 + x2^2) = 2^24 + 2; n = 5 is
+    # (x0^2 + x1^2) + (x2^2 + (x3^2 + x4^2)) = 2^24 + 3 -> 2^24 + 4
+    ("n3", [2.0 ** 12, 1.0, 1.0], 2.0 ** 24 + 2),
+    ("n5", [2.0 ** 12, 1.0, 1.0, 1.0, 1.0], 2.0 ** 24 + 4),
+    ("n1", [-3.0], 9.0),
+    # x = [2^12, 0 x 254, 1, 1, 0 x 255]: the ones at dims 255 and 256 lie in
+    # different halves; [0, 256) = 2^24 + 1 -> 2^24, [256, 512) = 1, and
+    # 2^24 + 1 -> 2^24.  (Right to left, or a split elsewhere than the middle,
+    # adds the two ones first: 2^24 + 2.)
+    ("split", [2.0 ** 12] + [0.0] * 254 + [1.0, 1.0] + [0.0] * 255, 2.0 ** 24),
+]
+
+
+@pytest.mark.parametrize("name,x,ss", PAIRWISE_CASES, ids=[c[0] for c in PAIRWISE_CASES])
+def test_sum_squares_pairwise_hand_derived(name, x, ss):
+    x = np.asarray(x, np.float32)
+    assert f32_bits(oracle.sum_squares(x, "pairwise")) == f32_bits(np.float32(ss))
+    if name not in ("n1", "split"):  # these tell pairwise from index order
+        assert f32_bits(oracle.sum_squares(x)) == f32_bits(np.float32(2.0 ** 24))
+
+
+@pytest.mark.parametrize("sum_order", ["index", "pairwise"])
+def test_rmsnorm_applies_its_sum(sum_order):
+    # the normalisation after the sum: mean = ss / 512, r = 1 / sqrt(mean +
+    # eps), y = x * r, each one fp32 rounding
+    rows = [np.asarray(PAIRWISE_CASES[0][1], np.float32),
+            np.asarray(PAIRWISE_CASES[1][1], np.float32)]
+    rows += [_head(seed, std=2.0) for seed in range(3)]
+    for x in rows:
+        r = _r_of_ss(oracle.sum_squares(x, sum_order))
+        y = oracle.rmsnorm_head(x, None, 1e-6, sum_order=sum_order)
+        assert (f32_bits(y) == f32_bits(x * r)).all()
+
+
+def test_rmsnorm_pairwise_order_hand_derived():
+    # x = [2^12, 0, 1, 1, 0 x 508] (the "pair" case): ss = 2^24 + 2 pairwise,
+    # 2^24 in index order, and the two give different r.
+    x = np.asarray(PAIRWISE_CASES[1][1], np.float32)
     r = _r_of_ss(2.0 ** 24 + 2)
-    y = oracle.rmsnorm_head(x, None, 1e-6, sum_order="tree")
-    assert f32_bits(y[1]) == f32_bits(np.float32(1.0) * r)
+    y = oracle.rmsnorm_head(x, None, 1e-6, sum_order="pairwise")
+    assert f32_bits(y[2]) == f32_bits(np.float32(1.0) * r)
+    assert f32_bits(y[0]) == f32_bits(np.float32(2.0 ** 12) * r)
     r_index = _r_of_ss(2.0 ** 24)
     assert r != r_index  # the test can tell the orders apart
-    assert f32_bits(oracle.rmsnorm_head(x, None, 1e-6)[1]) == f32_bits(r_index)
+    assert f32_bits(oracle.rmsnorm_head(x, None, 1e-6)[2]) == f32_bits(r_index)
 
 
-@pytest.mark.parametrize("sum_order", ["index", "tree"])
+@pytest.mark.parametrize("sum_order", ["index", "pairwise"])
 def test_rmsnorm_orders_exact_on_exact_sums(sum_order):
     # Small integers: every square and every partial sum is an exact fp32
     # integer, so any order gives the exact sum, and both orders agree bit for
