@@ -102,6 +102,15 @@ def assert_bits_equal(got, exp, what):
 # nearly cancel.
 Q_RTOL = 2.0 ** -15
 
+# On the forward workloads (8192 tokens x 64 heads with a norm weight, and
+# slices of them) the q paths may also differ from the definition's rounding
+# in at most 1e-3 of the bf16 values and 1e-4 of the e4m3 codes.  Without a
+# weight, or with a large eps, r cancels out of the codes to first order and
+# far more values sit on rounding midpoints, so these counts are asserted on
+# those workloads only.
+Q_DEF_FRAC_BF16 = 1e-3
+Q_DEF_FRAC_CODES = 1e-4
+
 
 def _q_slack(z):
     """Per element of fp32 q values z [..., 512]: the derived bound on how far
@@ -163,11 +172,12 @@ def _outside(z, lo, hi):
     return np.maximum(np.maximum(lo - z, z - hi), 0.0)
 
 
-def assert_bf16_near_definition(got, z_def, exp, what):
+def assert_bf16_near_definition(got, z_def, exp, what, max_frac=None):
     """q-path bf16 rows of the live heads against the oracle's definition:
     where a value differs from the definition's rounding `exp`, the
     definition's fp32 value z_def must lie within the derived slack of the
-    interval of reals that round to the value written."""
+    interval of reals that round to the value written.  With max_frac, at
+    most that fraction of the values may differ at all."""
     got = np.asarray(got, np.uint16).reshape(-1, 512)
     exp = np.asarray(exp, np.uint16).reshape(-1, 512)
     z = np.asarray(z_def, np.float32).reshape(-1, 512)
@@ -184,18 +194,22 @@ def assert_bf16_near_definition(got, z_def, exp, what):
           f"{far} by more than one ulp), each within the summation-order slack of its "
           f"rounding boundary", flush=True)
     assert (off <= slack).all(), f"{what}: {int((off > slack).sum())} differences unexplained"
+    if max_frac is not None:
+        assert n <= max_frac * got.size, f"{what}: {n / got.size:.2e} of the values differ"
 
 
-def assert_q_out_parity(got, q, w, pos, cache, hpad, eps, what):
+def assert_q_out_parity(got, q, w, pos, cache, hpad, eps, what, max_frac=None):
     """QNR bf16 rows: pad heads exact, live heads within the derived slack of
-    the RMSNorm definition, and bit for bit the oracle with the kernel's
-    summation order (pairwise)."""
+    the RMSNorm definition (and, with max_frac, differing from it in at most
+    that fraction of the values), and bit for bit the oracle with the
+    kernel's summation order (pairwise)."""
     got = np.asarray(got, np.uint16)
     exp = oracle.qnorm_rope(q, w, pos, cache, hpad, eps)
     hq = q.shape[1]
     assert_bits_equal(got[:, hq:], exp[:, hq:], f"{what} pad heads")
     z = oracle.qnorm_rope_f32(q, w, pos, cache, eps)
-    assert_bf16_near_definition(got[:, :hq], z, exp[:, :hq], f"{what} vs index-order RMSNorm")
+    assert_bf16_near_definition(got[:, :hq], z, exp[:, :hq], f"{what} vs index-order RMSNorm",
+                                max_frac)
     exp_pw = oracle.qnorm_rope(q, w, pos, cache, hpad, eps, sum_order="pairwise")
     assert_bits_equal(got, exp_pw, f"{what} vs pairwise-summed RMSNorm")
 
@@ -210,13 +224,14 @@ def _scales_f32(sc, fmt):
     return None, sc.view(np.float32).reshape(-1, 4).astype(np.float64)
 
 
-def assert_fp8_near_definition(codes, sc, z_def, ec, es, fmt, what):
+def assert_fp8_near_definition(codes, sc, z_def, ec, es, fmt, what, max_frac=None):
     """FP8 q path of the live heads against the oracle's definition: block
     scales within Q_RTOL (UE8M0: exponent bytes within one), and where a code
     differs from the definition's, the definition's fp32 value scaled by the
     written block's own multiplier must lie within the derived slack (plus
     two fp32 roundings) of the interval of values that encode to the written
-    code."""
+    code.  With max_frac, at most that fraction of the codes may differ at
+    all."""
     ge, gs = _scales_f32(sc, fmt)
     ee, xs = _scales_f32(es, fmt)
     assert gs.shape == xs.shape
@@ -242,12 +257,16 @@ def assert_fp8_near_definition(codes, sc, z_def, ec, es, fmt, what):
           f"codes ({n / gc.size:.2e}) differ from the definition, each within the "
           f"summation-order slack of its rounding boundary", flush=True)
     assert (off <= slack[d]).all(), f"{what}: {int((off > slack[d]).sum())} codes unexplained"
+    if max_frac is not None:
+        assert n <= max_frac * gc.size, f"{what}: {n / gc.size:.2e} of the codes differ"
 
 
-def assert_q_fp8_parity(codes, sc, q, w, pos, cache, hpad, eps, fmt, what, quant_eps=1e-10):
+def assert_q_fp8_parity(codes, sc, q, w, pos, cache, hpad, eps, fmt, what, quant_eps=1e-10,
+                        max_frac=None):
     """FP8 q path: pad heads exact, live heads within the derived slack of the
-    definition, and bit for bit (codes to the code bar) the oracle with the
-    kernel's summation order (pairwise)."""
+    definition (and, with max_frac, differing from it in at most that
+    fraction of the codes), and bit for bit (codes to the code bar) the
+    oracle with the kernel's summation order (pairwise)."""
     f = oracle.SCALE_UE8M0 if fmt == "ue8m0" else oracle.SCALE_FP32
     codes = np.asarray(codes, np.uint8)
     sc = np.asarray(sc)
@@ -257,7 +276,7 @@ def assert_q_fp8_parity(codes, sc, q, w, pos, cache, hpad, eps, fmt, what, quant
     assert_bits_equal(sc[:, hq:], es[:, hq:], f"{what} pad-head scales")
     z = oracle.qnorm_rope_f32(q, w, pos, cache, eps)
     assert_fp8_near_definition(codes[:, :hq], sc[:, :hq], z, ec[:, :hq], es[:, :hq], fmt,
-                               f"{what} vs index-order RMSNorm")
+                               f"{what} vs index-order RMSNorm", max_frac)
     ec, es = oracle.qnorm_rope_fp8(q, w, pos, cache, hpad, eps, f, quant_eps,
                                    sum_order="pairwise")
     assert_bits_equal(sc, es, f"{what} scales vs pairwise-summed RMSNorm")
