@@ -921,6 +921,97 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
   qnr_body<HAS_WEIGHT, OUT>(p, wave_index(p.hdr), lds + 256 * (threadIdx.x >> 6));
 }
 
+// qnorm_rope (bf16 q_out) for a few tokens: one head per wave, so that a
+// wave's own instruction latency, which sets the time of a call this small,
+// covers one head instead of four (108 VALU instructions per wave against
+// qnr_kernel's 387).  Lane l holds dims 8l .. 8l+7, read by one 16-byte load
+// and written by one 16-byte store: no LDS.  The sum of squares is the same
+// pairwise tree as rms_inv's: dims 8l .. 8l+7 in the lane (levels 1-3), then
+// lanes l ^ 1, l ^ 2 (quad DPP), the row halves and rows of 16 (row mirrors,
+// on values already uniform over the quads and halves), then l ^ 16 and
+// l ^ 32 (ds_bpermute); every lane ends with the same bits.  The rotated dims
+// 448..511 are lanes 56..63, GPT-J pairs 4(l - 56) .. 4(l - 56) + 3.  Every
+// other operation is qnr_body's, in its order, so the two kernels write the
+// same bits ([P3] section 5 RMSNorm, then forward RoPE, bf16 RNE; pad heads
+// +0 [P1] section 1).
+template <bool HAS_WEIGHT>
+__global__ __launch_bounds__(256) void qnr1_kernel(QnrParams p) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t u =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if (u >= p.units) return;
+  const uint32_t t = magic_div(u, p.div_hpad);
+  const uint32_t h = u - t * p.hpad;
+  uint4 outw = make_uint4(0u, 0u, 0u, 0u);  // pad head: +0
+  if (h < p.hq) {
+    const int64_t pos = load_uniform(p.positions + t);
+    const uint4 raw =
+        reinterpret_cast<const uint4*>(p.q + (int64_t)t * p.q_st + (int64_t)h * p.q_sh)[lane];
+    uint4 wt = make_uint4(0u, 0u, 0u, 0u);
+    if (HAS_WEIGHT) wt = reinterpret_cast<const uint4*>(p.weight)[lane];
+    const bool bad = pos < 0 || pos >= p.max_pos;
+    // cos / sin of the lane's pairs (lanes 56..63; the others read a row
+    // they do not use)
+    const float4* csrow = reinterpret_cast<const float4*>(p.cs + (bad ? 0 : pos) * 64);
+    const int pr = lane >= 56 ? lane - 56 : (lane & 7);
+    const float4 c4 = csrow[pr], s4 = csrow[8 + pr];
+    float x[8];
+    const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf_lo(d[i]);
+      x[2 * i + 1] = bf_hi(d[i]);
+    }
+    float sq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq[e] = x[e] * x[e];
+    float ss = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+    ss = ss + dpp_f32<kQuadSwap1>(ss);
+    ss = ss + dpp_f32<kQuadSwap2>(ss);
+    ss = ss + dpp_f32<kRowHalfMirror>(ss);
+    ss = ss + dpp_f32<kRowMirror>(ss);
+    ss = ss + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                            4 * (lane ^ 16), __builtin_bit_cast(int, ss)));
+    ss = ss + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                            4 * (lane ^ 32), __builtin_bit_cast(int, ss)));
+    const float mean = ss * (1.0f / 512.0f);
+    const float rs = recip_scale(sqrtf(mean + p.eps));  // as rms_inv
+    if (HAS_WEIGHT) {
+      const uint32_t wd[4] = {wt.x, wt.y, wt.z, wt.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = (x[2 * i] * rs) * bf_lo(wd[i]);
+        x[2 * i + 1] = (x[2 * i + 1] * rs) * bf_hi(wd[i]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * rs;
+    }
+    if (lane >= 56) {  // forward GPT-J rotation, as rope_lane<false>
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = x[2 * i], o = x[2 * i + 1];
+        const float ec = e * cv[i], os = o * sv[i], oc = o * cv[i], es = e * sv[i];
+        x[2 * i] = ec - os;
+        x[2 * i + 1] = oc + es;
+      }
+    }
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 f = {x[2 * i], x[2 * i + 1]};
+      o4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    // a position outside the table: the head is written as NaN
+    outw = bad ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u)
+               : make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  }
+  reinterpret_cast<uint4*>(p.q_out + (int64_t)u * kHeadDim)[lane] = outw;
+}
+
 struct KviParams {
   LaunchHdr hdr;
   const uint16_t* kv;
@@ -1472,6 +1563,8 @@ int launch(const void* fn, uint32_t units, LaunchShape shape, void* params,
 constexpr LaunchShape kIrqShape{6, 256};  // FP8 codes, two units per wave
 constexpr LaunchShape kIrbShape{6, 256};  // bf16 rows
 constexpr LaunchShape kQnrShape{4, 256};  // bf16 q_out
+constexpr uint32_t kQnrOneHeadUnits = 2048;      // qnorm_rope: one head per wave up to here
+constexpr uint32_t kQnrOneHeadSmallUnits = 512;  // ... in 64-thread workgroups up to here
 constexpr LaunchShape kQf8Shape{4, 256};  // FP8 q_out
 constexpr LaunchShape kFusedShape{4, 256};
 constexpr LaunchShape kKviShape{4, 256};
@@ -1735,6 +1828,23 @@ const void* qnr_fn(bool has_weight) {
   return has_weight ? (const void*)qnr_kernel<true, QOUT> : (const void*)qnr_kernel<false, QOUT>;
 }
 
+// qnorm_rope's entry for few heads (decode): qnr1_kernel, one head per
+// wave, 64-thread workgroups up to 512 heads (the waves spread over the most
+// CUs) and 256-thread ones above.  Per call in a HIP graph on MI355X, 32
+// heads padded to 128: 1.94 against 2.50 us at 1 token, 2.26 against 2.65 at
+// 16; from 32 tokens on, the thousands of single-head waves cost more to
+// launch than they save and qnr_kernel takes over.
+int launch_qnr1(QnrParams& p, bool has_weight, void* stream) {
+  const uint32_t threads = p.units <= kQnrOneHeadSmallUnits ? 64u : 256u;
+  const uint32_t per_block = threads / 64u;
+  void* args[] = {&p};
+  const void* fn =
+      has_weight ? (const void*)qnr1_kernel<true> : (const void*)qnr1_kernel<false>;
+  const hipError_t e = hipLaunchKernel(fn, dim3((p.units + per_block - 1u) / per_block),
+                                       dim3(threads), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
 template <int QOUT, int KOUT>
 const void* fused_fn(bool has_weight) {
   return has_weight ? (const void*)fused_qnr_kvi_kernel<true, QOUT, KOUT>
@@ -1765,6 +1875,7 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
                           cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps,
                           kOutBf16, q_out, nullptr, nullptr, 0.0, p, empty);
   if (rc != RQ_OK || empty) return rc;
+  if (p.units <= kQnrOneHeadUnits) return launch_qnr1(p, norm_weight != nullptr, stream);
   return launch(qnr_fn<kOutBf16>(norm_weight != nullptr), p.units, kQnrShape, &p,
                 (hipStream_t)stream);
 }

@@ -58,6 +58,24 @@ def test_qnr_decode_sizes(N):
     qnr_check(q, w, pos, synth.cos_sin_cache(65536), 128, 1e-6, "decode")
 
 
+@pytest.mark.parametrize("weighted", [True, False])
+def test_qnr_launch_table_entries_bit_identical(weighted):
+    # 613 tokens x 24 heads padded to 32 (19616 heads) take qnorm_rope's
+    # prefill entry.  The same tokens in calls of 1280 and 320 heads take the
+    # one-head-per-wave entry (256- and 64-thread workgroups), and calls of
+    # 4800 and 13216 heads the four-head entry in 64-thread workgroups.
+    cfg = dict(synth.QNR_FORWARD, N=613, Hq=24, Hpad=32, max_pos=65536, seed=34)
+    q, w, _, cache = synth.qnr_inputs(cfg)
+    w = w if weighted else None
+    pos = synth.uniform_positions(613, 65536, 34)
+    print(f"[case] qnr launch-table entries weighted={weighted}", flush=True)
+    full = qnr_gpu(q, w, pos, cache, 32, 1e-6)
+    assert_q_out_parity(full, q, w, pos, cache, 32, 1e-6, "qnr prefill entry")
+    for t0, t1 in ((0, 40), (40, 50), (50, 200), (200, 613)):
+        part = qnr_gpu(q[t0:t1].copy(), w, pos[t0:t1].copy(), cache, 32, 1e-6)
+        assert (part == full[t0:t1]).all(), f"tokens {t0}..{t1} differ from the prefill entry"
+
+
 def test_qnr_strided_input():
     cfg = dict(synth.QNR_FORWARD, N=21, Hq=12, Hpad=16, seed=32)
     q, w, pos, cache = synth.qnr_inputs(cfg)
