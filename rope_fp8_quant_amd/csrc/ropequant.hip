@@ -712,6 +712,99 @@ __global__ __launch_bounds__(256) void irq_kernel(IrqParams p) {
   }
 }
 
+// inv_rope_fp8_quant for a few tokens: one head per wave, so that a wave's
+// own instruction latency, which sets the time of a call this small, covers
+// one head instead of two.  Lane l holds dims 8l .. 8l+7 (one 16-byte load,
+// no LDS); quant block b is the lanes of DPP row b, its maximum four DPP
+// steps; the rotated dims 448..511 are lanes 56..63, GPT-J pairs
+// 4(l - 56) .. 4(l - 56) + 3.  Every value is computed by irq_kernel's
+// operations in its order (inverse rotation [P4] section 2, block scale and
+// codes [P4] section 3), so both kernels write the same bits.  Lane l stores
+// codes 8l .. 8l+7 of the head's row; the first lane gathers the four block
+// scales (readlane) and stores them as irq_kernel does.
+template <int FMT>
+__global__ __launch_bounds__(256) void irq1_kernel(IrqParams p) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t u =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if (u >= p.units) return;
+  const uint32_t t = magic_div(u, p.div_heads);
+  const uint32_t hh = u - t * p.n_heads;
+  const uint32_t g = magic_div(hh, p.div_hpg);
+  const uint32_t j = hh - g * p.hpg;
+  const int64_t pos = load_uniform(p.positions + t);
+  const uint4 raw =
+      reinterpret_cast<const uint4*>(p.o + (int64_t)t * p.o_st + (int64_t)hh * p.o_sh)[lane];
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  // cos / sin of the lane's pairs (lanes 56..63; the others read a row they
+  // do not use)
+  const float4* csrow = reinterpret_cast<const float4*>(p.cs + (bad ? 0 : pos) * 64);
+  const int pr = lane >= 56 ? lane - 56 : (lane & 7);
+  const float4 c4 = csrow[pr], s4 = csrow[8 + pr];
+  float x[8];
+  const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf_lo(d[i]);
+    x[2 * i + 1] = bf_hi(d[i]);
+  }
+  if (lane >= 56) {  // inverse GPT-J rotation: e' = e*c + o*s, o' = o*c - e*s
+    const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = x[2 * i], o = x[2 * i + 1];
+      const float ec = e * cv[i], os = o * sv[i], oc = o * cv[i], es = e * sv[i];
+      x[2 * i] = ec + os;
+      x[2 * i + 1] = oc - es;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
+  m = max_dpp_nonneg<kQuadSwap1>(m);
+  m = max_dpp_nonneg<kQuadSwap2>(m);
+  m = max_dpp_nonneg<kRowHalfMirror>(m);
+  m = max_dpp_nonneg<kRowMirror>(m);
+  float scale, mult;
+  uint32_t ebyte;
+  block_scale<FMT>(m, p.eps, scale, mult, ebyte);
+  uint32_t code[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float q0 = x[4 * hf] * mult, q1 = x[4 * hf + 1] * mult;
+    const float q2 = x[4 * hf + 2] * mult, q3 = x[4 * hf + 3] * mult;
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, __builtin_bit_cast(int, q0), false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, wd, true);
+    code[hf] = (uint32_t)wd;
+  }
+  uint8_t* const row = p.out + (int64_t)g * p.out_sg + (int64_t)t * p.out_st + (int64_t)j * kHeadDim;
+  reinterpret_cast<uint2*>(row)[lane] = make_uint2(code[0], code[1]);
+  // scales of the head; a position outside the table gives NaN scales
+  const int64_t first = (int64_t)g * p.sc_sg + (int64_t)t * p.sc_st +
+                        (int64_t)(FMT == RQ_SCALE_UE8M0 ? j : 4 * j) * p.sc_sb;
+  uint8_t* const sc = static_cast<uint8_t*>(p.scales) + 4 * first;
+  if (FMT == RQ_SCALE_UE8M0) {
+    const uint32_t wd = ebyte << (8 * (lane >> 4));
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)wd, 0) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 16) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 48);
+    if (lane == 0) *reinterpret_cast<uint32_t*>(sc) = bad ? 0xFFFFFFFFu : word;
+  } else {
+    const float sv = bad ? __builtin_nanf("") : scale;
+    if (p.sc_vec4) {
+      const int sb = __builtin_bit_cast(int, sv);
+      const uint4 s4v = make_uint4((uint32_t)__builtin_amdgcn_readlane(sb, 0),
+                                   (uint32_t)__builtin_amdgcn_readlane(sb, 16),
+                                   (uint32_t)__builtin_amdgcn_readlane(sb, 32),
+                                   (uint32_t)__builtin_amdgcn_readlane(sb, 48));
+      if (lane == 0) *reinterpret_cast<uint4*>(sc) = s4v;
+    } else if ((lane & 15) == 0) {
+      reinterpret_cast<float*>(sc)[(int64_t)(lane >> 4) * p.sc_sb] = sv;
+    }
+  }
+}
+
 struct QnrParams {
   LaunchHdr hdr;
   const uint16_t* q;
@@ -1486,7 +1579,9 @@ struct LaunchShape {
 // units (prefill): the kernel's prefill workgroup size (256 threads for
 // every kernel now), plenty of workgroups per CU.  Few units (decode):
 // 64-thread workgroups, one wave each, so the work spreads over as many CUs
-// as possible.  Results do not depend on the choice.
+// as possible; inv_rope_fp8_quant and qnorm_rope switch to their
+// one-head-per-wave kernels there instead (launch_one_head).  Results do not
+// depend on the choice.
 int pick_block_threads(uint32_t units, int prefill_threads) {
   return units >= 16384u ? prefill_threads : 64;
 }
@@ -1563,13 +1658,34 @@ int launch(const void* fn, uint32_t units, LaunchShape shape, void* params,
 constexpr LaunchShape kIrqShape{6, 256};  // FP8 codes, two units per wave
 constexpr LaunchShape kIrbShape{6, 256};  // bf16 rows
 constexpr LaunchShape kQnrShape{4, 256};  // bf16 q_out
-constexpr uint32_t kQnrOneHeadUnits = 2048;      // qnorm_rope: one head per wave up to here
-constexpr uint32_t kQnrOneHeadSmallUnits = 512;  // ... in 64-thread workgroups up to here
+constexpr uint32_t kQnrOneHeadUnits = 2048;  // qnorm_rope: one head per wave up to here
+constexpr uint32_t kIrqOneHeadUnits = 16383;  // inv_rope_fp8_quant: below the prefill entry
+constexpr uint32_t kOneHeadSmallUnits = 512;  // ... in 64-thread workgroups up to here
 constexpr LaunchShape kQf8Shape{4, 256};  // FP8 q_out
 constexpr LaunchShape kFusedShape{4, 256};
 constexpr LaunchShape kKviShape{4, 256};
 constexpr uint32_t kKviNtTokens = 4096;  // kv_rope_quant_insert: nontemporal record stores from here
 constexpr LaunchShape kIdxShape{4, 256};
+
+// The launch-table entry for few heads (decode): a one-head-per-wave kernel
+// (qnr1_kernel, irq1_kernel), in 64-thread workgroups up to 512 heads (the
+// waves spread over the most CUs) and 256-thread ones above.  Per call in a
+// HIP graph on MI355X:
+//   qnorm_rope, 32 heads padded to 128: 1.94 against 2.50 us (four heads per
+//   wave) at 1 token, 2.26 against 2.65 at 16; from 32 tokens on, the
+//   thousands of single-head waves (most of them pad heads) cost more to
+//   launch than they save, and the four-head kernel takes over;
+//   inv_rope_fp8_quant, 32 heads: 1.93 against 2.09 us (two heads per wave)
+//   at 1 token, 2.62 against 2.78 at 128, 5.35 against 5.77 at 511, so it
+//   takes every call below the prefill entry.
+int launch_one_head(const void* fn, void* params, uint32_t units, void* stream) {
+  const uint32_t threads = units <= kOneHeadSmallUnits ? 64u : 256u;
+  const uint32_t per_block = threads / 64u;
+  void* args[] = {params};
+  const hipError_t e = hipLaunchKernel(fn, dim3((units + per_block - 1u) / per_block),
+                                       dim3(threads), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
 
 bool finite_f32(double v) {
   const float f = (float)v;
@@ -1642,6 +1758,11 @@ int inv_rope_fp8_quant(const uint16_t* o, int64_t o_stride_token, int64_t o_stri
   p.scales = scales; p.sc_sg = sc_stride_group; p.sc_st = sc_stride_token; p.sc_sb = sc_stride_block;
   p.sc_vec4 = scale_fmt == RQ_SCALE_FP32 && sc_stride_block == 1 && sc_stride_group % 4 == 0 &&
               sc_stride_token % 4 == 0 && aligned(scales, 16);
+  if (p.units <= kIrqOneHeadUnits) {
+    const void* fn1 = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq1_kernel<RQ_SCALE_UE8M0>
+                                                  : (const void*)irq1_kernel<RQ_SCALE_FP32>;
+    return launch_one_head(fn1, &p, p.units, stream);
+  }
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? (const void*)irq_kernel<RQ_SCALE_UE8M0>
                                                : (const void*)irq_kernel<RQ_SCALE_FP32>;
   return launch(fn, p.units, kIrqShape, &p, (hipStream_t)stream, 2);
@@ -1828,23 +1949,6 @@ const void* qnr_fn(bool has_weight) {
   return has_weight ? (const void*)qnr_kernel<true, QOUT> : (const void*)qnr_kernel<false, QOUT>;
 }
 
-// qnorm_rope's entry for few heads (decode): qnr1_kernel, one head per
-// wave, 64-thread workgroups up to 512 heads (the waves spread over the most
-// CUs) and 256-thread ones above.  Per call in a HIP graph on MI355X, 32
-// heads padded to 128: 1.94 against 2.50 us at 1 token, 2.26 against 2.65 at
-// 16; from 32 tokens on, the thousands of single-head waves cost more to
-// launch than they save and qnr_kernel takes over.
-int launch_qnr1(QnrParams& p, bool has_weight, void* stream) {
-  const uint32_t threads = p.units <= kQnrOneHeadSmallUnits ? 64u : 256u;
-  const uint32_t per_block = threads / 64u;
-  void* args[] = {&p};
-  const void* fn =
-      has_weight ? (const void*)qnr1_kernel<true> : (const void*)qnr1_kernel<false>;
-  const hipError_t e = hipLaunchKernel(fn, dim3((p.units + per_block - 1u) / per_block),
-                                       dim3(threads), args, 0, (hipStream_t)stream);
-  return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
-}
-
 template <int QOUT, int KOUT>
 const void* fused_fn(bool has_weight) {
   return has_weight ? (const void*)fused_qnr_kvi_kernel<true, QOUT, KOUT>
@@ -1875,7 +1979,10 @@ int qnorm_rope(const uint16_t* q_in, int64_t q_stride_token, int64_t q_stride_he
                           cos_sin_cache, max_pos, n_tokens, n_heads_q, q_head_padded, eps,
                           kOutBf16, q_out, nullptr, nullptr, 0.0, p, empty);
   if (rc != RQ_OK || empty) return rc;
-  if (p.units <= kQnrOneHeadUnits) return launch_qnr1(p, norm_weight != nullptr, stream);
+  if (p.units <= kQnrOneHeadUnits)
+    return launch_one_head(norm_weight != nullptr ? (const void*)qnr1_kernel<true>
+                                                  : (const void*)qnr1_kernel<false>,
+                           &p, p.units, stream);
   return launch(qnr_fn<kOutBf16>(norm_weight != nullptr), p.units, kQnrShape, &p,
                 (hipStream_t)stream);
 }

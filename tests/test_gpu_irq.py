@@ -76,7 +76,8 @@ def test_irq_decode_sizes(N):
 @pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
 def test_irq_launch_table_entries_bit_identical(scale_fmt):
     # 613 tokens x 32 heads take the prefill entry of the launch table; the
-    # same tokens in two calls of under 512 tokens take the 64-thread entry
+    # same tokens in two calls of under 512 tokens take the one-head-per-wave
+    # entry (256-thread workgroups; decode sizes use its 64-thread ones)
     cfg = dict(synth.IRQ_TINY, N=613, H=32, hpg=8, max_pos=65536, seed=77)
     o, pos, cache = synth.irq_inputs(cfg)
     print(f"[case] irq launch-table entries {scale_fmt}", flush=True)
