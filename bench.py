@@ -688,6 +688,15 @@ def bench_decode(args, device, stream):
         def qnr():
             rq.qnorm_rope(q, None, pd, cache, q_out, 1e-6)
 
+        # the decode step's q + kv op [P1]: the same q, and the token's kv
+        # into a 4 x 64-slot paged cache at seeded slots
+        kvd = to_dev(synth.normal_bf16((N, 512), 60 + N, synth.T_KV), device)
+        sd = to_dev(synth.slot_permutation(N, 256, 60 + N), device)
+        kc = rq.empty_kv_cache(4, 64, device, fill=0xAA)
+
+        def fused():
+            rq.qnorm_rope_kv_rope_quant_insert(q, None, kvd, pd, cache, sd, q_out, kc, 64, 1e-6)
+
         ms = time_launches(irq, 200, 20, stream)
         msq = time_launches(qnr, 200, 20, stream)
         irq_p = rq.prepare(rq.inv_rope_fp8_quant, od, pd, cache, 8, out, sc)
@@ -695,6 +704,7 @@ def bench_decode(args, device, stream):
         msp = time_launches(irq_p, 200, 20, stream)
         msqp = time_launches(qnr_p, 200, 20, stream)
         gi, gq = graph_per_call_us(irq), graph_per_call_us(qnr)
+        gf = graph_per_call_us(fused)
         ci, cq = cold_single_us(irq, scratch), cold_single_us(qnr, scratch)
         res[f"N{N}"] = dict(irq_us_python=round(ms * 1e3, 2),
                             irq_us_prepared=round(msp * 1e3, 2), irq_us_graph=round(gi, 2),
@@ -703,7 +713,8 @@ def bench_decode(args, device, stream):
                             qnr_us_python=round(msq * 1e3, 2),
                             qnr_us_prepared=round(msqp * 1e3, 2), qnr_us_graph=round(gq, 2),
                             qnr_gbs_graph=round(qnr_bytes(N, 32, 128) / gq / 1e3, 1),
-                            qnr_us_single_cold=round(cq, 2))
+                            qnr_us_single_cold=round(cq, 2),
+                            qnr_kvi_fused_us_graph=round(gf, 2))
     del scratch
     return res
 

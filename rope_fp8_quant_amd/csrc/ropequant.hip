@@ -1028,11 +1028,8 @@ __global__ __launch_bounds__(256) void qnr_kernel(QnrParams p) {
 // same bits ([P3] section 5 RMSNorm, then forward RoPE, bf16 RNE; pad heads
 // +0 [P1] section 1).
 template <bool HAS_WEIGHT>
-__global__ __launch_bounds__(256) void qnr1_kernel(QnrParams p) {
+__device__ __forceinline__ void qnr1_body(const QnrParams& p, uint32_t u) {
   const int lane = threadIdx.x & 63;
-  const uint32_t u =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  if (u >= p.units) return;
   const uint32_t t = magic_div(u, p.div_hpad);
   const uint32_t h = u - t * p.hpad;
   uint4 outw = make_uint4(0u, 0u, 0u, 0u);  // pad head: +0
@@ -1103,6 +1100,18 @@ __global__ __launch_bounds__(256) void qnr1_kernel(QnrParams p) {
                : make_uint4(o4[0], o4[1], o4[2], o4[3]);
   }
   reinterpret_cast<uint4*>(p.q_out + (int64_t)u * kHeadDim)[lane] = outw;
+}
+
+// Wave index of the one-head-per-wave kernels (no XCD dealing: their
+// launches are a few hundred waves), made wave-uniform.
+__device__ __forceinline__ uint32_t flat_wave_index() {
+  return __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+}
+
+template <bool HAS_WEIGHT>
+__global__ __launch_bounds__(256) void qnr1_kernel(QnrParams p) {
+  const uint32_t u = flat_wave_index();
+  if (u < p.units) qnr1_body<HAS_WEIGHT>(p, u);
 }
 
 struct KviParams {
@@ -1336,6 +1345,89 @@ __global__ __launch_bounds__(256) void kvi2_kernel(KviParams p) {
   kvi2_body<FMT, NT>(p, wave_index(p.hdr), lds + 128 * (threadIdx.x >> 6));
 }
 
+// kv_rope_quant_insert for a few tokens: one token per wave, the layout of
+// irq1_kernel (lane l holds dims 8l .. 8l+7, quant block b = DPP row b, the
+// rotated dims on lanes 56..63) with kvi2_body's operations in its order:
+// forward RoPE, block scale and codes ([P4] sections 2-3), and the 528-byte
+// record at the token's slot [P1] section 1 (codes 8l .. 8l+7 from lane l,
+// the 16-byte scale tail from the first lane; plain stores: a decode step
+// reads the cache right after).  A slot outside the cache, or negative,
+// writes nothing; a position outside the table gives NaN scales.
+template <int FMT>
+__device__ __forceinline__ void kvi1_body(const KviParams& p, uint32_t t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t slot = load_uniform(p.slots + t);
+  const int64_t pos = load_uniform(p.positions + t);
+  const uint4 raw = reinterpret_cast<const uint4*>(p.kv + (int64_t)t * p.kv_st)[lane];
+  const bool bad = pos < 0 || pos >= p.max_pos;
+  const float4* csrow = reinterpret_cast<const float4*>(p.cs + (bad ? 0 : pos) * 64);
+  const int pr = lane >= 56 ? lane - 56 : (lane & 7);
+  const float4 c4 = csrow[pr], s4 = csrow[8 + pr];
+  float x[8];
+  const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf_lo(d[i]);
+    x[2 * i + 1] = bf_hi(d[i]);
+  }
+  if (lane >= 56) {  // forward GPT-J rotation: e' = e*c - o*s, o' = o*c + e*s
+    const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = x[2 * i], o = x[2 * i + 1];
+      const float ec = e * cv[i], os = o * sv[i], oc = o * cv[i], es = e * sv[i];
+      x[2 * i] = ec - os;
+      x[2 * i + 1] = oc + es;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
+  m = max_dpp_nonneg<kQuadSwap1>(m);
+  m = max_dpp_nonneg<kQuadSwap2>(m);
+  m = max_dpp_nonneg<kRowHalfMirror>(m);
+  m = max_dpp_nonneg<kRowMirror>(m);
+  float scale, mult;
+  uint32_t ebyte;
+  block_scale<FMT>(m, p.eps, scale, mult, ebyte);
+  uint32_t code[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float q0 = x[4 * hf] * mult, q1 = x[4 * hf + 1] * mult;
+    const float q2 = x[4 * hf + 2] * mult, q3 = x[4 * hf + 3] * mult;
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, __builtin_bit_cast(int, q0), false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, wd, true);
+    code[hf] = (uint32_t)wd;
+  }
+  uint4 tail;
+  if (FMT == RQ_SCALE_UE8M0) {
+    const uint32_t wd = ebyte << (8 * (lane >> 4));
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)wd, 0) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 16) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wd, 48);
+    tail = make_uint4(bad ? 0xFFFFFFFFu : word, 0u, 0u, 0u);
+  } else {
+    const int sb = bad ? 0x7FC00000 : __builtin_bit_cast(int, scale);
+    tail = make_uint4((uint32_t)__builtin_amdgcn_readlane(sb, 0),
+                      (uint32_t)__builtin_amdgcn_readlane(sb, 16),
+                      (uint32_t)__builtin_amdgcn_readlane(sb, 32),
+                      (uint32_t)__builtin_amdgcn_readlane(sb, 48));
+  }
+  if (slot < 0 || slot >= p.num_slots) return;  // padding token, or no such slot
+  const uint32_t blk_i = magic_div((uint32_t)slot, p.div_bs);
+  const uint32_t idx = (uint32_t)slot - blk_i * p.bs;
+  uint8_t* const rec = p.cache + (int64_t)blk_i * p.block_stride + (int64_t)idx * kRecordBytes;
+  reinterpret_cast<uint2*>(rec)[lane] = make_uint2(code[0], code[1]);
+  if (lane == 0) *reinterpret_cast<uint4*>(rec + kHeadDim) = tail;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void kvi1_kernel(KviParams p) {
+  const uint32_t t = flat_wave_index();
+  if (t < p.n_tokens) kvi1_body<FMT>(p, t);
+}
+
 // The q path and the kv path in one launch ([P1] section 1: the op
 // normalizes and rotates q and inserts the rotated kv in a single kernel;
 // section 2 names the full-cache forms: q as bf16 (in place) or FP8, kv into
@@ -1364,6 +1456,19 @@ __global__ __launch_bounds__(256) void fused_qnr_kvi_kernel(FusedParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   } else {
     qnr_body<HAS_WEIGHT, QOUT>(p.q, w, lds_wave);
+  }
+}
+
+// qnorm_rope_kv_rope_quant_insert for a few tokens: the decode kernels' one
+// head (q) or one token (kv) per wave, q waves first.  The two paths share
+// nothing but the positions, so each wave runs one body.
+template <bool HAS_WEIGHT, int KFMT>
+__global__ __launch_bounds__(256) void fused1_kernel(FusedParams p) {
+  const uint32_t w = flat_wave_index();
+  if (w < p.q.units) {
+    qnr1_body<HAS_WEIGHT>(p.q, w);
+  } else if (w - p.q.units < p.k.n_tokens) {
+    kvi1_body<KFMT>(p.k, w - p.q.units);
   }
 }
 
@@ -1660,24 +1765,31 @@ constexpr LaunchShape kIrbShape{6, 256};  // bf16 rows
 constexpr LaunchShape kQnrShape{4, 256};  // bf16 q_out
 constexpr uint32_t kQnrOneHeadUnits = 2048;  // qnorm_rope: one head per wave up to here
 constexpr uint32_t kIrqOneHeadUnits = 16383;  // inv_rope_fp8_quant: below the prefill entry
-constexpr uint32_t kOneHeadSmallUnits = 512;  // ... in 64-thread workgroups up to here
+constexpr uint32_t kOneHeadSmallUnits = 512;  // ... in 64-thread workgroups up to here (waves)
 constexpr LaunchShape kQf8Shape{4, 256};  // FP8 q_out
 constexpr LaunchShape kFusedShape{4, 256};
 constexpr LaunchShape kKviShape{4, 256};
+constexpr uint32_t kKviOneTokenTokens = 2048;  // kv_rope_quant_insert: one token per wave
 constexpr uint32_t kKviNtTokens = 4096;  // kv_rope_quant_insert: nontemporal record stores from here
 constexpr LaunchShape kIdxShape{4, 256};
 
 // The launch-table entry for few heads (decode): a one-head-per-wave kernel
-// (qnr1_kernel, irq1_kernel), in 64-thread workgroups up to 512 heads (the
-// waves spread over the most CUs) and 256-thread ones above.  Per call in a
-// HIP graph on MI355X:
+// (qnr1_kernel, irq1_kernel, kvi1_kernel, fused1_kernel), in 64-thread
+// workgroups up to 512 waves (they spread over the most CUs) and 256-thread
+// ones above.  Per call in a HIP graph on MI355X:
 //   qnorm_rope, 32 heads padded to 128: 1.94 against 2.50 us (four heads per
 //   wave) at 1 token, 2.26 against 2.65 at 16; from 32 tokens on, the
 //   thousands of single-head waves (most of them pad heads) cost more to
 //   launch than they save, and the four-head kernel takes over;
 //   inv_rope_fp8_quant, 32 heads: 1.93 against 2.09 us (two heads per wave)
 //   at 1 token, 2.62 against 2.78 at 128, 5.35 against 5.77 at 511, so it
-//   takes every call below the prefill entry.
+//   takes every call below the prefill entry;
+//   kv_rope_quant_insert (kvi1_kernel, one token per wave): 1.67 against
+//   1.74 us (two tokens per wave) at 1 token, 2.04 against 2.19 at 1024; it
+//   takes calls of up to 2048 tokens, below the size where the records'
+//   stores turn nontemporal;
+//   qnorm_rope_kv_rope_quant_insert (fused1_kernel) with the q path's entry:
+//   1.94 against 2.63 us at 1 token, 2.31 against 3.02 at 16.
 int launch_one_head(const void* fn, void* params, uint32_t units, void* stream) {
   const uint32_t threads = units <= kOneHeadSmallUnits ? 64u : 256u;
   const uint32_t per_block = threads / 64u;
@@ -2017,6 +2129,10 @@ int kv_rope_quant_insert(const uint16_t* kv, int64_t kv_stride_token, const int6
                           n_tokens, k_cache, num_blocks, block_stride_bytes, cache_block_size,
                           scale_fmt, eps, p, empty);
   if (rc != RQ_OK || empty) return rc;
+  if (p.n_tokens <= kKviOneTokenTokens)
+    return launch_one_head(scale_fmt == RQ_SCALE_UE8M0 ? (const void*)kvi1_kernel<RQ_SCALE_UE8M0>
+                                                       : (const void*)kvi1_kernel<RQ_SCALE_FP32>,
+                           &p, p.n_tokens, stream);
   const bool nt = p.n_tokens >= kKviNtTokens;
   const void* fn = scale_fmt == RQ_SCALE_UE8M0
                        ? (nt ? (const void*)kvi2_kernel<RQ_SCALE_UE8M0, true>
@@ -2058,6 +2174,14 @@ int qnorm_rope_kv_rope_quant_insert(
                 p.k, ek);
   if (rc != RQ_OK || eq) return rc;  // both are empty exactly when n_tokens == 0
   const bool w = norm_weight != nullptr;
+  if (p.q.units <= kQnrOneHeadUnits) {
+    const bool ue = scale_fmt == RQ_SCALE_UE8M0;
+    const void* fn1 = w ? (ue ? (const void*)fused1_kernel<true, RQ_SCALE_UE8M0>
+                              : (const void*)fused1_kernel<true, RQ_SCALE_FP32>)
+                        : (ue ? (const void*)fused1_kernel<false, RQ_SCALE_UE8M0>
+                              : (const void*)fused1_kernel<false, RQ_SCALE_FP32>);
+    return launch_one_head(fn1, &p, p.q.units + p.k.n_tokens, stream);
+  }
   const void* fn = scale_fmt == RQ_SCALE_UE8M0 ? fused_fn<kOutBf16, RQ_SCALE_UE8M0>(w)
                                                : fused_fn<kOutBf16, RQ_SCALE_FP32>(w);
   return launch_fused(fn, p, stream, 2);

@@ -163,6 +163,31 @@ def test_kvi_holes_gaps_and_out_of_range(shape):
               f"holes {shape}", oracle_slots=o_slots)
 
 
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_kvi_launch_table_entries_bit_identical(scale_fmt):
+    # 4500 tokens take the two-token kernel with nontemporal record stores;
+    # the same tokens in calls of 2048 and 300 take the one-token kernel
+    # (256- and 64-thread workgroups), and a call of 2152 the two-token
+    # kernel with plain stores.  Every call writes the same cache bytes.
+    N, bs = 4500, 64
+    nb = -(-N // bs) + 3
+    kv = synth.normal_bf16((N, 512), 36, synth.T_KV)
+    pos = synth.uniform_positions(N, 65536, 36)
+    slots = synth.slot_permutation(N, nb * bs, 36)
+    slots[[5, 2100, 4400]] = -1
+    cache = synth.cos_sin_cache(65536)
+    print(f"[case] kvi launch-table entries fmt={scale_fmt}", flush=True)
+    full = kvi_check(kv, pos, cache, slots, nb, bs, None, scale_fmt, "one call")
+    parts = np.full_like(full, 0xAA)
+    for t0, t1 in ((0, 2048), (2048, 2348), (2348, 4500)):
+        part = kvi_gpu(kv[t0:t1].copy(), pos[t0:t1].copy(), cache, slots[t0:t1].copy(), nb, bs,
+                       bs * 528, scale_fmt)
+        touched = part != 0xAA
+        parts[touched] = part[touched]
+    # a record byte that happens to equal 0xAA stays as the fill in `parts`
+    assert (parts == full).all(), "the split calls wrote different cache bytes"
+
+
 @pytest.mark.parametrize("N", [4095, 4096])
 @pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
 def test_kvi_store_policy_threshold(N, scale_fmt):
